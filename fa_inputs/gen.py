@@ -1,0 +1,104 @@
+"""Seeded input generator (see the package docstring for the recipe)."""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# Draw order of the seven tensors.  U_Q, U_K, U_V are the upstream cotangents
+# on dQ, dK, dV (called gdQ, gdK, gdV in the workload descriptions).
+NAMES = ("q", "k", "v", "do", "uq", "uk", "uv")
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "bf16" or "fp32": the element type the kernels receive
+    seed: int
+    cot_std: float = 1.0  # standard deviation of U_Q, U_K, U_V
+    qk_gain: float = 1.0  # extra factor on Q and K rows (peaked softmax rows)
+    causal: bool = False
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    @property
+    def bob_flops(self) -> float:
+        """Algorithmic flops of one BoB call: 19 N x N x d contractions per head.
+
+        Row pass: S, F (two products), dP, C, then four accumulations that
+        contract over the key index with two products each for gdO and the
+        Omega term plus one each for R and B (11 in all).  Column pass: S, F
+        (two), dP, C, then gK (two) and gV (one), 8 in all.  Each contraction
+        is 2 N^2 d flops, so 38 B H N^2 d for non-causal attention.
+        """
+        return 38.0 * self.B * self.H * self.N * self.N * self.d
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 128, 64, "fp32", 0,
+                     note="fp32 inputs; parity against the float64 oracle"),
+    "mid": Workload("mid", 2, 8, 4096, 64, "bf16", 1),
+    "hd128": Workload("hd128", 1, 16, 16384, 128, "bf16", 2, cot_std=0.1),
+    "long": Workload("long", 1, 4, 65536, 64, "bf16", 3, qk_gain=2.0),
+    "max": Workload("max", 1, 1, 262144, 64, "bf16", 4),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    r = (u + np.uint32(0x7FFF) + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
+                cot_std: float = 1.0, qk_gain: float = 1.0):
+    """Draw the seven inputs.
+
+    Returns ``(raw, f64)``: ``raw`` maps each name to the array the device
+    receives (uint16 bf16 bits, or float32), ``f64`` maps each name to the
+    same values as float64 for the oracle.
+    """
+    if dtype not in ("bf16", "fp32"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    raw, f64 = {}, {}
+    for name in NAMES:
+        x = rng.standard_normal(size=(B, H, N, d), dtype=np.float32)
+        if name in ("uq", "uk", "uv") and cot_std != 1.0:
+            x = (x * np.float32(cot_std)).astype(np.float32)
+        if name in ("q", "k") and qk_gain != 1.0:
+            x = (x * np.float32(qk_gain)).astype(np.float32)
+        if dtype == "bf16":
+            bits = f32_to_bf16_bits(x)
+            raw[name] = bits
+            f64[name] = bf16_bits_to_f32(bits).astype(np.float64)
+        else:
+            raw[name] = x
+            f64[name] = x.astype(np.float64)
+    return raw, f64
+
+
+def workload_inputs(w: Workload, N: int | None = None):
+    """Inputs of a named workload (optionally with a different length N)."""
+    return make_inputs(w.B, w.H, w.N if N is None else N, w.d, w.seed, w.dtype,
+                       w.cot_std, w.qk_gain)
