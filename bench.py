@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of exact attention backward-over-backward (fa_bob) on one MI355X.
+
+A step is one fa_bob call: the row-scalar kernel (D = rowsum(dO * O)), the
+row-major pass and the column-major pass, on inputs already resident in HBM.
+fa_fwd (which supplies O and L) runs once before the timed region and is
+reported separately, as is fa_bwd.
+
+Throughput: 38 B H N^2 d flops per step (19 N x N x d contractions per head:
+11 in the row pass, 8 in the column pass) divided by the step time, in
+TFLOP/s.  The default workload is "mid" (B=2, H=8, N=4096, d=64, bf16); the
+other bf16 workloads (N = 16K, 64K, 262K) are timed as a sweep in the same
+JSON line.
+
+Per-kernel times come from HIP events recorded on the launch stream between
+the three kernels of each timed step (fa_bob_phase 0, 1, 2 in order is
+exactly fa_bob).  The dominant kernel is the row pass (22 of the 38 flops).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_FP32_MFMA_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bob_pass1_traffic.json")
+KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_kernels.hip", "exact_second_order_fa_amd/csrc/fa_tile.h")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def device_inputs(w):
+    import torch
+
+    from fa_inputs import workload_inputs
+
+    raw, _ = workload_inputs(w)
+    out = {}
+    for k, v in raw.items():
+        if w.dtype == "bf16":
+            out[k] = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            out[k] = torch.from_numpy(v).cuda()
+    return out
+
+
+class Runner:
+    """Inputs, saved forward state and preallocated outputs of one workload."""
+
+    def __init__(self, w):
+        import torch
+
+        import exact_second_order_fa_amd as fa
+
+        self.fa, self.w = fa, w
+        self.t = device_inputs(w)
+        shape = (w.B, w.H, w.N, w.d)
+        self.o, self.lse = fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"])
+        self.outs = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(4)]
+        code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP32
+        self.ws = torch.empty(fa.bob_workspace_bytes(*shape, code) // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def bob(self, phase=None):
+        t, g = self.t, self.outs
+        self.fa.fa_bob(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], t["uq"], t["uk"], t["uv"],
+                       gq=g[0], gk=g[1], gv=g[2], gdo=g[3], ws=self.ws, phase=phase)
+
+    def fwd(self):
+        self.fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], o=self.o, lse=self.lse)
+
+
+def time_steps(r, steps, warmup):
+    """Warmup, then `steps` timed steps.  Returns (wall ms/step, per-kernel
+    average ms from HIP events recorded on the launch stream)."""
+    import torch
+
+    for _ in range(warmup):
+        r.bob()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for ph in range(3):
+            r.bob(phase=ph)
+            ev[s][ph + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [float(np.mean([ev[s][ph].elapsed_time(ev[s][ph + 1]) for s in range(steps)])) for ph in range(3)]
+    step_ev = float(np.mean([ev[s][0].elapsed_time(ev[s][3]) for s in range(steps)]))
+    return wall, step_ev, per
+
+
+def time_plain(fn, reps):
+    import torch
+
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def traffic_for(workload):
+    """Per-launch HBM bytes of the row pass from the committed rocprofv3
+    counter summary, or None when missing or taken on other kernel code."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_source_sha() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, heads):
+    """The float64 oracle on a bounded sample (the first `heads` heads of the
+    workload, full row and column passes), scaled to TFLOP/s in the same
+    38 N^2 d accounting."""
+    from fa_inputs import workload_inputs
+    from oracle import col_pass, row_pass
+
+    _, f64 = workload_inputs(w)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    done = 0
+    t0 = time.perf_counter()
+    for bh in range(heads):
+        b, h = divmod(bh, w.H)
+        a = [f64[n][b, h] for n in ("q", "k", "v", "do", "uq", "uk", "uv")]
+        r = row_pass(*a, w.scale, outputs="all", threads=threads)
+        col_pass(*a, w.scale, r, threads=threads)
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = 38.0 * done * w.N * w.N * w.d
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.H} heads of workload {w.name} (N={w.N}, d={w.d}), full row and "
+                      f"column passes in float64, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mid")
+    ap.add_argument("--sweep", default="hd128,long,max", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the kernel runs on one GPU's share of the "
+              "heads and --gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from fa_inputs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    r = Runner(w)
+    wall, step_ev, per = time_steps(r, args.steps, args.warmup)
+    bob_ms = time_plain(r.bob, args.steps)
+    fwd_ms = time_plain(r.fwd, max(3, args.steps // 4))
+    flops = w.bob_flops
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    value = flops / (wall * 1e9)
+    pass1_flops = 22.0 * w.B * w.H * w.N * w.N * w.d
+    ach = pass1_flops / (per[1] * 1e9)
+    traffic = traffic_for(w.name)
+
+    sweep = {}
+    for name in [s for s in args.sweep.split(",") if s]:
+        sw = WORKLOADS[name]
+        del r
+        torch.cuda.empty_cache()
+        r = Runner(sw)
+        reps = 3 if sw.N >= 65536 else 10
+        _, s_ev, s_per = time_steps(r, reps, 1)
+        tf = sw.bob_flops / (s_ev * 1e9)
+        sweep[name] = {"B": sw.B, "H": sw.H, "N": sw.N, "d": sw.d, "ms": round(s_ev, 3),
+                       "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "pass1_ms": round(s_per[1], 3), "pass2_ms": round(s_per[2], 3),
+                       "rowscalar_ms": round(s_per[0], 4)}
+
+    line = {
+        "metric": "fa_bob TFLOP/s (38 B H N^2 d flops per call) and fraction of bf16 dense MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, see fa_inputs)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False,
+                   "in_dtype": w.dtype, "scale": "1/sqrt(d)"},
+        "frac_peak": round(value / peak, 4),
+        "roofline": {"bound": "mfma", "kernel": "bob_pass1 (row pass)", "achieved": round(ach, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                     "traffic": traffic, "flops_per_launch": pass1_flops},
+        "kernels_ms": {"rowscalar": round(per[0], 4), "bob_pass1": round(per[1], 4),
+                       "bob_pass2": round(per[2], 4), "step_events": round(step_ev, 4),
+                       "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)},
+        "sweep": sweep,
+    }
+    if not args.no_cpu:
+        nh = w.B * w.H if args.cpu_heads <= 0 else min(args.cpu_heads, w.B * w.H)
+        line["cpu_baseline"] = cpu_baseline(w, nh)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

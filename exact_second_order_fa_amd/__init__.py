@@ -1,0 +1,233 @@
+"""Python binding of the gfx950 attention library (``libfa.so``, C ABI in
+``include/fa.h``): forward, first backward and exact backward-over-backward
+of softmax attention.
+
+This layer only marshals arguments: it checks tensor shapes and dtypes,
+allocates outputs with PyTorch on the inputs' device (the library itself
+never allocates), and passes raw device pointers, element strides and the
+current HIP stream to the C entry points.  Every step of the computation runs
+in the HIP kernels; there is no fallback path.  If the shared library is
+missing the calls raise ``FaLibraryError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_STRIDE", 4: "FA_ERR_DTYPE",
+    5: "FA_ERR_UNSUPPORTED", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP",
+}
+FA_BF16, FA_FP32 = 0, 1
+
+# Exported symbols (kept equal to the declarations in include/fa.h).
+SYMBOLS = ("fa_version", "fa_status_str", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
+           "fa_bob_workspace_bytes", "fa_bob", "fa_bob_phase")
+
+
+class FaLibraryError(RuntimeError):
+    pass
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+class FaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d", ctypes.c_int64), ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int32)]
+
+
+class FaTensor(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+_LIB = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None and path is None:
+        return _LIB
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FaLibraryError(f"{p} is not built; run `python -m exact_second_order_fa_amd.build` "
+                             "(hipcc, gfx950) first")
+    lib = ctypes.CDLL(p)
+    P, T, vp, sz = ctypes.POINTER(FaProblem), FaTensor, ctypes.c_void_p, ctypes.c_size_t
+    lib.fa_version.restype = ctypes.c_int
+    lib.fa_version.argtypes = []
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.argtypes = [P]
+    lib.fa_bob_workspace_bytes.restype = sz
+    lib.fa_bob_workspace_bytes.argtypes = [P]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [P, T, T, T, T, vp, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [P, T, T, T, T, vp, T, T, T, T, vp, sz, vp]
+    lib.fa_bob.restype = ctypes.c_int
+    lib.fa_bob.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, vp]
+    lib.fa_bob_phase.restype = ctypes.c_int
+    lib.fa_bob_phase.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, ctypes.c_int32, vp]
+    if path is None:
+        _LIB = lib
+    return lib
+
+
+def version() -> int:
+    return load_library().fa_version()
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(int(status)).decode()
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def problem(B, H, N, d, in_dtype=FA_BF16, scale=None, causal=0) -> FaProblem:
+    return FaProblem(int(B), int(H), int(N), int(d), float(-1.0 if scale is None else scale),
+                     int(causal), int(in_dtype))
+
+
+def tensor_arg(t) -> FaTensor:
+    """An fa_tensor for a [B, H, N, d] torch tensor with a contiguous last dim."""
+    if t.dim() != 4:
+        raise ValueError(f"expected a [B, H, N, d] tensor, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    return FaTensor(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_FP32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_inputs(*ts):
+    first = ts[0]
+    for t in ts:
+        if t.shape != first.shape or t.dtype != first.dtype or t.device != first.device:
+            raise ValueError("q, k, v, dout and the cotangents must share shape, dtype and device")
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+    return first.shape
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _f32_like(x, out):
+    torch = _torch()
+    if out is not None:
+        if out.dtype != torch.float32 or out.shape != x.shape:
+            raise ValueError("outputs must be float32 with the inputs' shape")
+        return out
+    return torch.empty(x.shape, dtype=torch.float32, device=x.device)
+
+
+def _call(name, status):
+    if status != FA_OK:
+        raise FaError(status, name)
+
+
+def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
+    """Forward: returns (O fp32 [B,H,N,d], L fp32 [B,H,N], natural-log
+    log-sum-exp of tau q.k over keys)."""
+    torch = _torch()
+    B, H, N, d = _check_inputs(q, k, v)
+    p = problem(B, H, N, d, _dtype_code(q), scale)
+    o = _f32_like(q, o)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _call("fa_fwd", load_library().fa_fwd(ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v),
+                                          tensor_arg(o), ctypes.c_void_p(lse.data_ptr()), _stream(stream)))
+    return o, lse
+
+
+def bwd_workspace_bytes(B, H, N, d, in_dtype=FA_BF16) -> int:
+    p = problem(B, H, N, d, in_dtype)
+    return int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
+
+
+def bob_workspace_bytes(B, H, N, d, in_dtype=FA_BF16) -> int:
+    p = problem(B, H, N, d, in_dtype)
+    return int(load_library().fa_bob_workspace_bytes(ctypes.byref(p)))
+
+
+def _workspace(nbytes, device, ws):
+    torch = _torch()
+    if ws is None:
+        return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    return ws
+
+
+def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None, stream=None):
+    """First backward: returns (dQ, dK, dV) fp32 and the workspace holding D."""
+    B, H, N, d = _check_inputs(q, k, v, dout)
+    p = problem(B, H, N, d, _dtype_code(q), scale)
+    dq, dk, dv = _f32_like(q, dq), _f32_like(q, dk), _f32_like(q, dv)
+    nbytes = int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
+    ws = _workspace(nbytes, q.device, ws)
+    _call("fa_bwd", load_library().fa_bwd(
+        ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+        ctypes.c_void_p(lse.data_ptr()), tensor_arg(dout), tensor_arg(dq), tensor_arg(dk),
+        tensor_arg(dv), ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size()),
+        _stream(stream)))
+    return dq, dk, dv, ws
+
+
+def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=None, gdo=None,
+           ws=None, stream=None, phase=None):
+    """Backward-over-backward: gradients of <dQ,U_Q> + <dK,U_K> + <dV,U_V> with
+    respect to Q, K, V and dO.  Returns (gQ, gK, gV, gdO, ws) with
+    ws = [D | alpha | E], each [B, H, N] fp32.  ``phase`` (0, 1 or 2) calls
+    fa_bob_phase instead, launching only that kernel."""
+    B, H, N, d = _check_inputs(q, k, v, dout, uq, uk, uv)
+    p = problem(B, H, N, d, _dtype_code(q), scale)
+    gq, gk, gv, gdo = (_f32_like(q, x) for x in (gq, gk, gv, gdo))
+    lib = load_library()
+    nbytes = int(lib.fa_bob_workspace_bytes(ctypes.byref(p)))
+    ws = _workspace(nbytes, q.device, ws)
+    args = [ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+            ctypes.c_void_p(lse.data_ptr()), tensor_arg(dout), tensor_arg(uq), tensor_arg(uk),
+            tensor_arg(uv), tensor_arg(gq), tensor_arg(gk), tensor_arg(gv), tensor_arg(gdo),
+            ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size())]
+    if phase is None:
+        _call("fa_bob", lib.fa_bob(*args, _stream(stream)))
+    else:
+        _call("fa_bob_phase", lib.fa_bob_phase(*args, ctypes.c_int32(phase), _stream(stream)))
+    return gq, gk, gv, gdo, ws
+
+
+def split_workspace(ws, B, H, N):
+    """Views D, alpha, E of a fa_bob workspace."""
+    n = B * H * N
+    return ws[:n].view(B, H, N), ws[n:2 * n].view(B, H, N), ws[2 * n:3 * n].view(B, H, N)

@@ -1,0 +1,320 @@
+// fa_api.hip -- the C ABI declared in include/fa.h: host-side validation and
+// kernel launches.  No allocation, no synchronisation, no state.
+#include <math.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_kernels.hip"
+
+namespace {
+
+using fa::Args;
+using fa::bf16;
+using fa::TDesc;
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+struct Ctx {
+  int64_t B, H, N, d;
+  size_t esize;  // input element size
+  bool bf;
+  float tau, pow2, rho;
+};
+
+fa_status check_problem(const fa_problem* p, Ctx* c) {
+  if (!p) return FA_ERR_NULL;
+  if (p->B < 1 || p->H < 1 || p->N < 1) return FA_ERR_SHAPE;
+  if (p->in_dtype != FA_BF16 && p->in_dtype != FA_FP32) return FA_ERR_DTYPE;
+  if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
+  if (p->causal != 0) return FA_ERR_UNSUPPORTED;
+  // fp32 inputs are built for d = 64 only (register budget of the fp32 MFMA path).
+  if (p->in_dtype == FA_FP32 && p->d != 64) return FA_ERR_UNSUPPORTED;
+  // Row vectors are indexed with 64-bit offsets, sequence positions and grid
+  // sizes with 32-bit ints.
+  if (p->N > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+  const int64_t bh = p->B * p->H;
+  if (p->B > (int64_t(1) << 30) || p->H > (int64_t(1) << 30) || bh > (int64_t(1) << 30)) return FA_ERR_SHAPE;
+  const int64_t nblk = (p->N + fa::kResRows - 1) / fa::kResRows;
+  if (bh * nblk > (int64_t(1) << 31) - 1) return FA_ERR_SHAPE;
+  if (bh * p->N > (int64_t(1) << 40)) return FA_ERR_SHAPE;
+  float tau = p->scale;
+  if (!(tau > 0.0f)) {
+    if (tau != tau) return FA_ERR_UNSUPPORTED;  // NaN
+    tau = 1.0f / sqrtf((float)p->d);
+  }
+  if (!isfinite(tau)) return FA_ERR_UNSUPPORTED;
+  int ex = 0;
+  const float m = frexpf(tau, &ex);  // tau = m * 2^ex, m in [0.5, 1)
+  c->B = p->B;
+  c->H = p->H;
+  c->N = p->N;
+  c->d = p->d;
+  c->bf = p->in_dtype == FA_BF16;
+  c->esize = c->bf ? 2 : 4;
+  c->tau = tau;
+  c->pow2 = ldexpf(1.0f, ex - 1);
+  c->rho = 2.0f * m;
+  if (!(c->pow2 > 0.0f) || !isfinite(c->pow2)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa_status check_tensor(const Ctx& c, const fa_tensor& t, size_t esize) {
+  if (!t.ptr) return FA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(t.ptr) % 16) return FA_ERR_STRIDE;
+  const int64_t vec = 16 / (int64_t)esize;
+  if (t.stride_n < c.d || t.stride_h < 0 || t.stride_b < 0) return FA_ERR_STRIDE;
+  if (t.stride_n % vec || t.stride_h % vec || t.stride_b % vec) return FA_ERR_STRIDE;
+  return FA_OK;
+}
+
+fa_status check_vec(const void* p) {
+  if (!p) return FA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(p) % 4) return FA_ERR_STRIDE;
+  return FA_OK;
+}
+
+TDesc desc(const fa_tensor& t) {
+  TDesc r;
+  r.p = t.ptr;
+  r.sb = t.stride_b;
+  r.sh = t.stride_h;
+  r.sn = t.stride_n;
+  return r;
+}
+
+Args base_args(const Ctx& c) {
+  Args a;
+  memset(&a, 0, sizeof(a));
+  a.B = (int)c.B;
+  a.H = (int)c.H;
+  a.N = (int)c.N;
+  a.tau = c.tau;
+  a.pow2 = c.pow2;
+  a.rho = c.rho;
+  a.c1 = fa::kLog2e * c.rho;
+  return a;
+}
+
+unsigned grid_rows(const Ctx& c) {
+  return (unsigned)(c.B * c.H * ((c.N + fa::kResRows - 1) / fa::kResRows));
+}
+
+unsigned grid_rowscalar(const Ctx& c) {
+  const int64_t rpb = 256 / (c.d / 8);
+  return (unsigned)((c.B * c.H * c.N + rpb - 1) / rpb);
+}
+
+#define FA_CHECK(x)                 \
+  do {                              \
+    const fa_status s_ = (x);       \
+    if (s_ != FA_OK) return s_;     \
+  } while (0)
+
+fa_status launched() { return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+template <typename T, int D>
+void launch_rowscalar(const Ctx& c, const Args& a, hipStream_t st) {
+  hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c)), dim3(256), 0, st, a);
+}
+
+// Streamed tile rows per LDS stage: one 16-byte register block per thread
+// for the bf16 path.
+template <typename T, int D>
+struct Tiles {
+  static constexpr int TS = (sizeof(T) == 2 && D == 64) ? 64 : 32;
+};
+
+template <typename T, int D>
+void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
+  hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+}
+
+template <typename T, int D>
+void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
+  launch_rowscalar<T, D>(c, a, st);
+  hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
+                     a);
+}
+
+// phase < 0: the whole BoB (row scalars, row pass, column pass); 0, 1, 2:
+// only that kernel.
+template <typename T, int D, bool RHO1>
+void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
+  if (phase < 0 || phase == 0) launch_rowscalar<T, D>(c, a, st);
+  if (phase < 0 || phase == 1)
+    hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads),
+                       0, st, a);
+  if (phase < 0 || phase == 2)
+    hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads),
+                       0, st, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return kVersion; }
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_SHAPE: return "invalid shape";
+    case FA_ERR_STRIDE: return "invalid stride or alignment";
+    case FA_ERR_DTYPE: return "invalid dtype";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+size_t fa_bwd_workspace_bytes(const fa_problem* p) {
+  Ctx c;
+  if (check_problem(p, &c) != FA_OK) return 0;
+  return (size_t)(c.B * c.H * c.N) * sizeof(float);
+}
+
+size_t fa_bob_workspace_bytes(const fa_problem* p) {
+  Ctx c;
+  if (check_problem(p, &c) != FA_OK) return 0;
+  return 3 * (size_t)(c.B * c.H * c.N) * sizeof(float);
+}
+
+fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
+                 void* stream) {
+  Ctx c;
+  FA_CHECK(check_problem(p, &c));
+  FA_CHECK(check_tensor(c, q, c.esize));
+  FA_CHECK(check_tensor(c, k, c.esize));
+  FA_CHECK(check_tensor(c, v, c.esize));
+  FA_CHECK(check_tensor(c, o, 4));
+  FA_CHECK(check_vec(lse));
+  Args a = base_args(c);
+  a.q = desc(q);
+  a.k = desc(k);
+  a.v = desc(v);
+  a.r0 = desc(o);
+  a.lse_out = lse;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (c.bf) {
+    if (c.d == 64) launch_fwd<bf16, 64>(c, a, st);
+    else launch_fwd<bf16, 128>(c, a, st);
+  } else {
+    launch_fwd<float, 64>(c, a, st);
+  }
+  return launched();
+}
+
+fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const float* lse,
+                 fa_tensor dout, fa_tensor dq, fa_tensor dk, fa_tensor dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  Ctx c;
+  FA_CHECK(check_problem(p, &c));
+  FA_CHECK(check_tensor(c, q, c.esize));
+  FA_CHECK(check_tensor(c, k, c.esize));
+  FA_CHECK(check_tensor(c, v, c.esize));
+  FA_CHECK(check_tensor(c, dout, c.esize));
+  FA_CHECK(check_tensor(c, o, 4));
+  FA_CHECK(check_tensor(c, dq, 4));
+  FA_CHECK(check_tensor(c, dk, 4));
+  FA_CHECK(check_tensor(c, dv, 4));
+  FA_CHECK(check_vec(lse));
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < fa_bwd_workspace_bytes(p)) return FA_ERR_WORKSPACE;
+  Args a = base_args(c);
+  a.q = desc(q);
+  a.k = desc(k);
+  a.v = desc(v);
+  a.o = desc(o);
+  a.dout = desc(dout);
+  a.r0 = desc(dq);
+  a.r1 = desc(dk);
+  a.r2 = desc(dv);
+  a.lse = lse;
+  a.D = reinterpret_cast<float*>(workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (c.bf) {
+    if (c.d == 64) launch_bwd<bf16, 64>(c, a, st);
+    else launch_bwd<bf16, 128>(c, a, st);
+  } else {
+    launch_bwd<float, 64>(c, a, st);
+  }
+  return launched();
+}
+
+static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o,
+                          const float* lse, fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq,
+                          fa_tensor gk, fa_tensor gv, fa_tensor gdo, void* workspace, size_t workspace_bytes,
+                          int phase, void* stream) {
+  Ctx c;
+  FA_CHECK(check_problem(p, &c));
+  FA_CHECK(check_tensor(c, q, c.esize));
+  FA_CHECK(check_tensor(c, k, c.esize));
+  FA_CHECK(check_tensor(c, v, c.esize));
+  FA_CHECK(check_tensor(c, dout, c.esize));
+  FA_CHECK(check_tensor(c, uq, c.esize));
+  FA_CHECK(check_tensor(c, uk, c.esize));
+  FA_CHECK(check_tensor(c, uv, c.esize));
+  FA_CHECK(check_tensor(c, o, 4));
+  FA_CHECK(check_tensor(c, gq, 4));
+  FA_CHECK(check_tensor(c, gk, 4));
+  FA_CHECK(check_tensor(c, gv, 4));
+  FA_CHECK(check_tensor(c, gdo, 4));
+  FA_CHECK(check_vec(lse));
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16) return FA_ERR_WORKSPACE;
+  if (workspace_bytes < fa_bob_workspace_bytes(p)) return FA_ERR_WORKSPACE;
+  Args a = base_args(c);
+  a.q = desc(q);
+  a.k = desc(k);
+  a.v = desc(v);
+  a.o = desc(o);
+  a.dout = desc(dout);
+  a.uq = desc(uq);
+  a.uk = desc(uk);
+  a.uv = desc(uv);
+  a.r0 = desc(gq);
+  a.r1 = desc(gk);
+  a.r2 = desc(gv);
+  a.r3 = desc(gdo);
+  a.lse = lse;
+  const size_t nrow = (size_t)(c.B * c.H * c.N);
+  a.D = reinterpret_cast<float*>(workspace);
+  a.alpha = a.D + nrow;
+  a.E = a.D + 2 * nrow;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const bool rho1 = c.rho == 1.0f;
+  if (c.bf) {
+    if (c.d == 64) {
+      if (rho1) launch_bob<bf16, 64, true>(c, a, st, phase);
+      else launch_bob<bf16, 64, false>(c, a, st, phase);
+    } else {
+      if (rho1) launch_bob<bf16, 128, true>(c, a, st, phase);
+      else launch_bob<bf16, 128, false>(c, a, st, phase);
+    }
+  } else {
+    if (rho1) launch_bob<float, 64, true>(c, a, st, phase);
+    else launch_bob<float, 64, false>(c, a, st, phase);
+  }
+  return launched();
+}
+
+fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const float* lse,
+                 fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq, fa_tensor gk, fa_tensor gv,
+                 fa_tensor gdo, void* workspace, size_t workspace_bytes, void* stream) {
+  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, -1, stream);
+}
+
+fa_status fa_bob_phase(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const float* lse,
+                       fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq, fa_tensor gk,
+                       fa_tensor gv, fa_tensor gdo, void* workspace, size_t workspace_bytes, int32_t phase,
+                       void* stream) {
+  if (phase < 0 || phase > 2) return FA_ERR_UNSUPPORTED;
+  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, phase, stream);
+}
+
+}  // extern "C"

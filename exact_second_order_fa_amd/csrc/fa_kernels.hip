@@ -1,0 +1,645 @@
+// fa_kernels.hip -- gfx950 kernels: forward, first backward, and the two-pass
+// exact backward-over-backward of softmax attention.
+//
+// Sources (page title, section):
+//   [FlashBoB]      "FlashBoB: I/O-Efficient Exact Backward-over-Backward for
+//                   Softmax Attention": section 3 (forward, L, first
+//                   backward), sections 4.2-4.3 (affine fusion, two-pass
+//                   schedule), appendix D (final assembled identities).
+//   [FA2-recompute] "Why does FlashAttention-2's backward pass recompute
+//                   attention ...": D = rowsum(dO * O), P = exp(S - L).
+//   [FA2-triton]    "FlashAttention-2 from PyTorch to Triton": online softmax
+//                   forward, masking of a ragged last key tile.
+//
+// Every kernel: 256 threads (4 waves), 32 resident rows per wave, streamed
+// tiles of TS rows double-buffered in LDS (see fa_tile.h for the operand
+// layouts).  The softmax scale is split as tau = pow2 * rho with pow2 an
+// exact power of two folded into the resident operands and rho in [1, 2)
+// applied in fp32 (rho == 1 at d = 64).
+#include "fa_tile.h"
+
+namespace fa {
+
+struct TDesc {
+  const void* p;
+  int64_t sb, sh, sn;
+};
+
+struct Args {
+  TDesc q, k, v, o, dout, uq, uk, uv;  // inputs (o: fp32)
+  TDesc r0, r1, r2, r3;                // outputs (fp32), kernel specific
+  const float* lse;                    // [B,H,N] saved log-normaliser (input)
+  float* lse_out;                      // [B,H,N] (fa_fwd output)
+  float* D;                            // [B,H,N] rowsum(dO * O)
+  float* alpha;                        // [B,H,N] BoB row scalar alpha
+  float* E;                            // [B,H,N] BoB row scalar E
+  int B, H, N;
+  float tau, pow2, rho, c1;  // c1 = log2(e) * rho
+};
+
+template <typename T>
+__device__ inline HeadPtr<T> head_of(const TDesc& t, int b, int h) {
+  HeadPtr<T> r;
+  r.p = reinterpret_cast<const T*>(t.p) + (int64_t)b * t.sb + (int64_t)h * t.sh;
+  r.sn = t.sn;
+  return r;
+}
+
+__device__ inline float* head_out(const TDesc& t, int b, int h) {
+  return reinterpret_cast<float*>(const_cast<void*>(t.p)) + (int64_t)b * t.sb + (int64_t)h * t.sh;
+}
+
+struct Work {
+  int bh, b, h, rb;
+};
+
+__device__ inline Work work_item(const Args& a) {
+  const int nblk = (a.N + kResRows - 1) / kResRows;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  Work r;
+  r.bh = w / nblk;
+  r.rb = w % nblk;
+  r.b = r.bh / a.H;
+  r.h = r.bh % a.H;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Row-scalar preprocessing: D_i = sum_c dO_ic O_ic ([FA2-recompute]; the
+// first backward's D_i = sum_j P_ij dP_ij).  HBM-bound: D/8 lanes per row,
+// eight elements each, reduced with lane shuffles.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rowscalar_kernel(Args a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int64_t total = (int64_t)a.B * a.H * a.N;
+  const int64_t gr = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c0 = (threadIdx.x % LPR) * 8;
+  float acc = 0.0f;
+  if (gr < total) {
+    const int64_t bh = gr / a.N;
+    const int i = (int)(gr % a.N);
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const HeadPtr<T> dout = head_of<T>(a.dout, b, h);
+    const HeadPtr<float> o = head_of<float>(a.o, b, h);
+    const T* dr = dout.p + (int64_t)i * dout.sn + c0;
+    const float* orow = o.p + (int64_t)i * o.sn + c0;
+    const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow);
+    const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 4);
+    float dv[8];
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(dr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dv[e] = (float)x[e];
+    } else {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(dr);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(dr + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dv[e] = x0[e];
+        dv[e + 4] = x1[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(dv[e], o0[e], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(dv[e + 4], o1[e], acc);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (gr < total && (threadIdx.x % LPR) == 0) a.D[gr] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Forward ([FlashBoB] section 3; online softmax as in [FA2-triton]).
+// Resident: 32 query rows per wave.  Streamed: K (row copy, for S^T = K Q^T)
+// and V (transposed copy, for O^T += V^T P^T).  Running max in base-2 units.
+template <typename T, int D, int TS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(Args a) {
+  typedef Elem<T> E;
+  typedef Stage<T, D, TS> S;
+  constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
+  __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<T> q = head_of<T>(a.q, wk.b, wk.h);
+  HeadPtr<T> src[2] = {head_of<T>(a.k, wk.b, wk.h), head_of<T>(a.v, wk.b, wk.h)};
+
+  typename E::frag qf[NKS];
+  load_resident<T, D>(qf, q.p, q.sn, row, N, a.pow2);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+  float m = -INFINITY, lsum = 0.0f;
+
+  Stager<T, D, TS, 2> st;
+  const int nt = (N + TS - 1) / TS;
+  st.load(src, 0, N);
+  st.store(lds[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    if (t + 1 < nt) st.load(src, (t + 1) * TS, N);
+    const T* kr = lds[t & 1];
+    const T* vt = lds[t & 1] + S::ELEMS + S::ROW_ELEMS;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, zero16());
+      const int j0 = t * TS + sub * 32;
+      const bool full = j0 + 32 <= N;
+      float z[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        z[idx] = s[idx] * a.c1;
+        if (!full && j0 + acc_pos(idx, hh) >= N) z[idx] = -INFINITY;
+        mx = fmaxf(mx, z[idx]);
+      }
+      mx = half_max(mx);
+      const float mn = fmaxf(m, mx);
+      const float ms = (mn == -INFINITY) ? 0.0f : mn;
+      const float sc = __builtin_amdgcn_exp2f(m - ms);
+      float p[16];
+      float ps = 0.0f;
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        p[idx] = __builtin_amdgcn_exp2f(z[idx] - ms);
+        ps += p[idx];
+      }
+      lsum = lsum * sc + ps;
+      m = mn;
+      Chain<T> cp;
+      cp.set(p);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] *= sc;
+#pragma unroll
+        for (int s2 = 0; s2 < KS32; ++s2) acc[db] = E::mma(tr_frag<T, D, TS>(vt, db, sub, s2), cp.f[s2], acc[db]);
+      }
+    }
+    if (t + 1 < nt) st.store(lds[(t + 1) & 1]);
+    __syncthreads();
+  }
+  const float lt = half_sum(lsum);
+  const float inv = 1.0f / lt;
+  float* o = head_out(a.r0, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_out(o, a.r0.sn, row, N, db, [&](int idx) { return acc[db][idx] * inv; });
+  if (row < N && hh == 0) a.lse_out[(int64_t)wk.bh * N + row] = kLn2 * (m + __log2f(lt));
+}
+
+// ---------------------------------------------------------------------------
+// First backward, row side: dQ = tau dS K with dS = P (dP - D)
+// ([FlashBoB] section 3).  Resident: query rows.  Streamed: K, V.
+template <typename T, int D, int TS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(Args a) {
+  typedef Elem<T> E;
+  typedef Stage<T, D, TS> S;
+  constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
+  __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<T> q = head_of<T>(a.q, wk.b, wk.h), dout = head_of<T>(a.dout, wk.b, wk.h);
+  HeadPtr<T> src[2] = {head_of<T>(a.k, wk.b, wk.h), head_of<T>(a.v, wk.b, wk.h)};
+
+  typename E::frag qf[NKS], df[NKS];
+  load_resident<T, D>(qf, q.p, q.sn, row, N, a.pow2);
+  load_resident<T, D>(df, dout.p, dout.sn, row, N, 1.0f);
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float Li = row < N ? a.lse[rv + row] : 0.0f;
+  const float Di = row < N ? a.D[rv + row] : 0.0f;
+  const float nl2 = -Li * kLog2e;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = zero16();
+
+  Stager<T, D, TS, 2> st;
+  const int nt = (N + TS - 1) / TS;
+  st.load(src, 0, N);
+  st.store(lds[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    if (t + 1 < nt) st.load(src, (t + 1) * TS, N);
+    const T* kr = lds[t & 1];
+    const T* kt = kr + S::ROW_ELEMS;
+    const T* vr = kr + S::ELEMS;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, zero16());
+      const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
+      const int j0 = t * TS + sub * 32;
+      const bool full = j0 + 32 <= N;
+      float ds[16];
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
+        if (!full && j0 + acc_pos(idx, hh) >= N) p = 0.0f;
+        ds[idx] = p * (dp[idx] - Di);
+      }
+      Chain<T> cds;
+      cds.set(ds);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < KS32; ++s2) acc[db] = E::mma(tr_frag<T, D, TS>(kt, db, sub, s2), cds.f[s2], acc[db]);
+    }
+    if (t + 1 < nt) st.store(lds[(t + 1) & 1]);
+    __syncthreads();
+  }
+  float* dq = head_out(a.r0, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_out(dq, a.r0.sn, row, N, db, [&](int idx) { return a.tau * acc[db][idx]; });
+}
+
+// Row scalars of a streamed tile, staged into LDS next to the operand tiles.
+// NS scalars per streamed row; Fn maps (global row) -> values.
+template <int TS, int NS>
+struct ScalarStager {
+  float v[NS];
+  bool active;
+  template <typename Fn>
+  __device__ inline void load(int row0, int N, Fn fn) {
+    active = threadIdx.x < TS;
+    if (active) {
+      const int row = row0 + threadIdx.x;
+      if (row < N) {
+        fn(row, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < NS; ++e) v[e] = 0.0f;
+      }
+    }
+  }
+  __device__ inline void store(float* lds) const {
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < NS; ++e) lds[e * TS + threadIdx.x] = v[e];
+    }
+  }
+};
+
+// Chain-initial value of a score-shaped accumulator from a staged per-row
+// scalar array: element idx gets sc[sub*32 + acc_pos(idx, hh)].
+template <int TS>
+__device__ inline f32x16 row_init(const float* sc, int sub) {
+  const int hh = lane_id() >> 5;
+  f32x16 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(sc + sub * 32 + sig(8 * b + 4 * hh));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * b + e] = x[e];
+  }
+  return r;
+}
+
+// First backward, column side: dV = P^T dO, dK = tau dS^T Q
+// ([FlashBoB] section 3).  Resident: key rows.  Streamed: Q, dO and the row
+// scalars (-L/rho, -D).
+template <typename T, int D, int TS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(Args a) {
+  typedef Elem<T> E;
+  typedef Stage<T, D, TS> S;
+  constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
+  __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
+  __shared__ __attribute__((aligned(16))) float scl[2][2 * TS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<T> k = head_of<T>(a.k, wk.b, wk.h), v = head_of<T>(a.v, wk.b, wk.h);
+  HeadPtr<T> src[2] = {head_of<T>(a.q, wk.b, wk.h), head_of<T>(a.dout, wk.b, wk.h)};
+
+  typename E::frag kf[NKS], vf[NKS];
+  load_resident<T, D>(kf, k.p, k.sn, col, N, a.pow2);
+  load_resident<T, D>(vf, v.p, v.sn, col, N, 1.0f);
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float irho = 1.0f / a.rho;
+  auto scal = [&](int row, float* o) {
+    o[0] = -a.lse[rv + row] * irho;
+    o[1] = -a.D[rv + row];
+  };
+
+  f32x16 ak[NDB], av[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) ak[db] = av[db] = zero16();
+
+  Stager<T, D, TS, 2> st;
+  ScalarStager<TS, 2> ss;
+  const int nt = (N + TS - 1) / TS;
+  st.load(src, 0, N);
+  ss.load(0, N, scal);
+  st.store(lds[0]);
+  ss.store(scl[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    if (t + 1 < nt) {
+      st.load(src, (t + 1) * TS, N);
+      ss.load((t + 1) * TS, N, scal);
+    }
+    const T* qr = lds[t & 1];
+    const T* qt = qr + S::ROW_ELEMS;
+    const T* dr = qr + S::ELEMS;
+    const T* dt = dr + S::ROW_ELEMS;
+    const float* sc = scl[t & 1];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, row_init<TS>(sc, sub));
+      const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
+      const int i0 = t * TS + sub * 32;
+      const bool full = i0 + 32 <= N;
+      float p[16], ds[16];
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        float pp = __builtin_amdgcn_exp2f(s[idx] * a.c1);
+        if (!full && i0 + acc_pos(idx, hh) >= N) pp = 0.0f;
+        p[idx] = pp;
+        ds[idx] = pp * dp[idx];
+      }
+      Chain<T> cp, cds;
+      cp.set(p);
+      cds.set(ds);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < KS32; ++s2) {
+          av[db] = E::mma(tr_frag<T, D, TS>(dt, db, sub, s2), cp.f[s2], av[db]);
+          ak[db] = E::mma(tr_frag<T, D, TS>(qt, db, sub, s2), cds.f[s2], ak[db]);
+        }
+    }
+    if (t + 1 < nt) {
+      st.store(lds[(t + 1) & 1]);
+      ss.store(scl[(t + 1) & 1]);
+    }
+    __syncthreads();
+  }
+  float* dk = head_out(a.r1, wk.b, wk.h);
+  float* dv = head_out(a.r2, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_out(dk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
+    store_out(dv, a.r2.sn, col, N, db, [&](int idx) { return av[db][idx]; });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// BoB pass 1 (row-major; [FlashBoB] section 4.3, Algorithm 1's first pass).
+// Resident per wave: 32 query rows i with q_i, u_Q,i (scaled by pow2), do_i,
+// and the row scalars L_i, D_i.  Streamed: K, V, U_K, U_V.  Per 32 x 32
+// tile (streamed index j on M):
+//   S^T = K Q^T,  F^T = K U_Q^T + U_K Q^T,  dP^T = V dO^T,  C^T = U_V dO^T
+//   P = exp(tau S - L),  dPD = dP - D,  P~ = C + F dPD   (d~P before the
+//   alpha correction), then the alpha-free accumulators of the affine
+//   fusion (section 4.2):
+//     alpha += sum_j P F            E° += sum_j P P~
+//     G     += P U_V + (P F) V      (d~(dO) before the correction)
+//     Om    += (P P~) K + dS U_K    with dS = P dPD
+//     R'    += dS K                 Bk += P K
+// Epilogue (the corrections of section 4.2, with R = R' + D Bk so that
+// alpha R + E Bk = alpha R' + E° Bk):
+//     E = E° - alpha D,  gdo = G - alpha o,  gq = tau (Om - alpha R' - E° Bk).
+template <typename T, int D, int TS, bool RHO1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_kernel(Args a) {
+  typedef Elem<T> E;
+  typedef Stage<T, D, TS> S;
+  constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
+  __shared__ __attribute__((aligned(16))) T lds[2][4 * S::ELEMS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<T> q = head_of<T>(a.q, wk.b, wk.h), uq = head_of<T>(a.uq, wk.b, wk.h),
+                   dout = head_of<T>(a.dout, wk.b, wk.h);
+  HeadPtr<T> src[4] = {head_of<T>(a.k, wk.b, wk.h), head_of<T>(a.v, wk.b, wk.h), head_of<T>(a.uk, wk.b, wk.h),
+                       head_of<T>(a.uv, wk.b, wk.h)};
+
+  typename E::frag qf[NKS], uqf[NKS], df[NKS];
+  load_resident<T, D>(qf, q.p, q.sn, row, N, a.pow2);
+  load_resident<T, D>(uqf, uq.p, uq.sn, row, N, a.pow2);
+  load_resident<T, D>(df, dout.p, dout.sn, row, N, 1.0f);
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float Li = row < N ? a.lse[rv + row] : 0.0f;
+  const float Di = row < N ? a.D[rv + row] : 0.0f;
+  const float nl2 = -Li * kLog2e;
+
+  f32x16 ag[NDB], aom[NDB], ar[NDB], abk[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) ag[db] = aom[db] = ar[db] = abk[db] = zero16();
+  float alpha_p = 0.0f, eo_p = 0.0f;
+
+  Stager<T, D, TS, 4> st;
+  const int nt = (N + TS - 1) / TS;
+  st.load(src, 0, N);
+  st.store(lds[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    if (t + 1 < nt) st.load(src, (t + 1) * TS, N);
+    const T* kr = lds[t & 1];
+    const T* kt = kr + S::ROW_ELEMS;
+    const T* vr = kr + S::ELEMS;
+    const T* vt = vr + S::ROW_ELEMS;
+    const T* ukr = kr + 2 * S::ELEMS;
+    const T* ukt = ukr + S::ROW_ELEMS;
+    const T* uvr = kr + 3 * S::ELEMS;
+    const T* uvt = uvr + S::ROW_ELEMS;
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, zero16());
+      f32x16 f = mm_row<T, D, TS>(kr, sub, uqf, zero16());
+      f = mm_row<T, D, TS>(ukr, sub, qf, f);
+      const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
+      const f32x16 c = mm_row<T, D, TS>(uvr, sub, df, zero16());
+      const int j0 = t * TS + sub * 32;
+      const bool full = j0 + 32 <= N;
+      float P[16], PF[16], PT[16], DS[16];
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
+        if (!full && j0 + acc_pos(idx, hh) >= N) p = 0.0f;
+        const float F = RHO1 ? f[idx] : f[idx] * a.rho;
+        const float dpd = dp[idx] - Di;
+        const float t0 = fmaf(F, dpd, c[idx]);
+        P[idx] = p;
+        PF[idx] = p * F;
+        PT[idx] = p * t0;
+        DS[idx] = p * dpd;
+        alpha_p += PF[idx];
+        eo_p += PT[idx];
+      }
+      Chain<T> cp, cpf, cpt, cds;
+      cp.set(P);
+      cpf.set(PF);
+      cpt.set(PT);
+      cds.set(DS);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < KS32; ++s2) {
+          const typename E::frag xuv = tr_frag<T, D, TS>(uvt, db, sub, s2);
+          const typename E::frag xv = tr_frag<T, D, TS>(vt, db, sub, s2);
+          const typename E::frag xk = tr_frag<T, D, TS>(kt, db, sub, s2);
+          const typename E::frag xuk = tr_frag<T, D, TS>(ukt, db, sub, s2);
+          ag[db] = E::mma(xuv, cp.f[s2], ag[db]);
+          ag[db] = E::mma(xv, cpf.f[s2], ag[db]);
+          aom[db] = E::mma(xk, cpt.f[s2], aom[db]);
+          aom[db] = E::mma(xuk, cds.f[s2], aom[db]);
+          ar[db] = E::mma(xk, cds.f[s2], ar[db]);
+          abk[db] = E::mma(xk, cp.f[s2], abk[db]);
+        }
+    }
+    if (t + 1 < nt) st.store(lds[(t + 1) & 1]);
+    __syncthreads();
+  }
+
+  const float alpha = half_sum(alpha_p);
+  const float eo = half_sum(eo_p);
+  if (row < N && hh == 0) {
+    a.alpha[rv + row] = alpha;
+    a.E[rv + row] = eo - alpha * Di;
+  }
+  const HeadPtr<float> o = head_of<float>(a.o, wk.b, wk.h);
+  float* gq = head_out(a.r0, wk.b, wk.h);
+  float* gdo = head_out(a.r3, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    float ov[16];
+    if (row < N) {
+      const float* orow = o.p + (int64_t)row * o.sn + db * 32 + 4 * hh;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(orow + 8 * b4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[4 * b4 + e] = x[e];
+      }
+    }
+    store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx] - alpha * ov[idx]; });
+    store_out(gq, a.r0.sn, row, N, db,
+              [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eo * abk[db][idx]); });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// BoB pass 2 (column-major; [FlashBoB] section 4.3, Algorithm 1's second
+// pass).  Resident per wave: 32 key rows j with k_j, u_K,j (scaled by pow2),
+// v_j, u_V,j.  Streamed: Q, dO, U_Q and the row scalars L, D, alpha, E,
+// staged as MFMA chain initial values -L/rho, -D, -alpha/rho,
+// -(alpha D + E).  Per tile (streamed index i on M):
+//   s = (tau S - L)/rho,  h/rho = (F - alpha)/rho,  dPD = dP - D,
+//   C' = C - alpha D - E,
+//   P = exp(tau S - L),   d~P - E = C' + h dPD,
+//   d~S = P (d~P - E),    dS = P dPD,    W = P h,
+//   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
+template <typename T, int D, int TS, bool RHO1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_kernel(Args a) {
+  typedef Elem<T> E;
+  typedef Stage<T, D, TS> S;
+  constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
+  __shared__ __attribute__((aligned(16))) T lds[2][3 * S::ELEMS];
+  __shared__ __attribute__((aligned(16))) float scl[2][4 * TS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<T> k = head_of<T>(a.k, wk.b, wk.h), v = head_of<T>(a.v, wk.b, wk.h),
+                   uk = head_of<T>(a.uk, wk.b, wk.h), uv = head_of<T>(a.uv, wk.b, wk.h);
+  HeadPtr<T> src[3] = {head_of<T>(a.q, wk.b, wk.h), head_of<T>(a.dout, wk.b, wk.h), head_of<T>(a.uq, wk.b, wk.h)};
+
+  typename E::frag kf[NKS], vf[NKS], ukf[NKS], uvf[NKS];
+  load_resident<T, D>(kf, k.p, k.sn, col, N, a.pow2);
+  load_resident<T, D>(ukf, uk.p, uk.sn, col, N, a.pow2);
+  load_resident<T, D>(vf, v.p, v.sn, col, N, 1.0f);
+  load_resident<T, D>(uvf, uv.p, uv.sn, col, N, 1.0f);
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float irho = 1.0f / a.rho;
+  auto scal = [&](int row, float* o) {
+    const float L = a.lse[rv + row], Dd = a.D[rv + row], al = a.alpha[rv + row], Ee = a.E[rv + row];
+    o[0] = -L * irho;
+    o[1] = -Dd;
+    o[2] = -al * irho;
+    o[3] = -fmaf(al, Dd, Ee);
+  };
+
+  f32x16 ak[NDB], av[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) ak[db] = av[db] = zero16();
+
+  Stager<T, D, TS, 3> st;
+  ScalarStager<TS, 4> ss;
+  const int nt = (N + TS - 1) / TS;
+  st.load(src, 0, N);
+  ss.load(0, N, scal);
+  st.store(lds[0]);
+  ss.store(scl[0]);
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    if (t + 1 < nt) {
+      st.load(src, (t + 1) * TS, N);
+      ss.load((t + 1) * TS, N, scal);
+    }
+    const T* qr = lds[t & 1];
+    const T* qt = qr + S::ROW_ELEMS;
+    const T* dr = qr + S::ELEMS;
+    const T* dt = dr + S::ROW_ELEMS;
+    const T* uqr = qr + 2 * S::ELEMS;
+    const T* uqt = uqr + S::ROW_ELEMS;
+    const float* sc = scl[t & 1];
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, row_init<TS>(sc, sub));
+      f32x16 f = mm_row<T, D, TS>(uqr, sub, kf, row_init<TS>(sc + 2 * TS, sub));
+      f = mm_row<T, D, TS>(qr, sub, ukf, f);
+      const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
+      const f32x16 c = mm_row<T, D, TS>(dr, sub, uvf, row_init<TS>(sc + 3 * TS, sub));
+      const int i0 = t * TS + sub * 32;
+      const bool full = i0 + 32 <= N;
+      float DT[16], DS[16], W[16];
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
+        if (!full && i0 + acc_pos(idx, hh) >= N) p = 0.0f;
+        const float h = RHO1 ? f[idx] : f[idx] * a.rho;
+        const float x = fmaf(h, dp[idx], c[idx]);
+        DT[idx] = p * x;
+        DS[idx] = p * dp[idx];
+        W[idx] = p * h;
+      }
+      Chain<T> cdt, cds, cw;
+      cdt.set(DT);
+      cds.set(DS);
+      cw.set(W);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < KS32; ++s2) {
+          ak[db] = E::mma(tr_frag<T, D, TS>(qt, db, sub, s2), cdt.f[s2], ak[db]);
+          ak[db] = E::mma(tr_frag<T, D, TS>(uqt, db, sub, s2), cds.f[s2], ak[db]);
+          av[db] = E::mma(tr_frag<T, D, TS>(dt, db, sub, s2), cw.f[s2], av[db]);
+        }
+    }
+    if (t + 1 < nt) {
+      st.store(lds[(t + 1) & 1]);
+      ss.store(scl[(t + 1) & 1]);
+    }
+    __syncthreads();
+  }
+  float* gk = head_out(a.r1, wk.b, wk.h);
+  float* gv = head_out(a.r2, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_out(gk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
+    store_out(gv, a.r2.sn, col, N, db, [&](int idx) { return av[db][idx]; });
+  }
+}
+
+}  // namespace fa

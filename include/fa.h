@@ -1,0 +1,164 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) attention library: forward, first
+ * backward and exact backward-over-backward (BoB) of softmax attention.
+ *
+ * Sources cited below by page title and section:
+ *   [FlashBoB]      "FlashBoB: I/O-Efficient Exact Backward-over-Backward for
+ *                   Softmax Attention" (Givans, Crawshaw, Liu).
+ *   [FA2-recompute] "Why does FlashAttention-2's backward pass recompute
+ *                   attention, and what exactly does the forward pass save
+ *                   for it?"
+ *   [FA2-triton]    "FlashAttention-2 from PyTorch to Triton".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Problem: B batches x H heads, sequence length N (queries = keys), head
+ * dimension d, softmax scale tau, non-causal.  One attention head is the
+ * (b, h) slice.
+ *
+ * Tensors: every N x d operand is passed as an fa_tensor: a DEVICE pointer
+ * plus element strides for the batch, head and sequence dimensions; the head
+ * dimension is contiguous (stride 1).  Element (b, h, n, c) lives at
+ * ptr[b*stride_b + h*stride_h + n*stride_n + c].  Pointers must be 16-byte
+ * aligned and stride_n, stride_h, stride_b must be multiples of 16 bytes
+ * (8 bf16 or 4 fp32 elements); stride_n >= d.  Inputs Q, K, V, dO, U_Q,
+ * U_K, U_V use the problem's input dtype (bf16 or fp32).  O and every
+ * output are fp32.
+ *
+ * Row vectors (L, and D / alpha / E in the workspace) are contiguous
+ * [B, H, N] fp32 device arrays.
+ *
+ * Ownership: the caller allocates and frees every buffer.  The library never
+ * allocates, frees or synchronises; it enqueues kernels on `stream` (a
+ * hipStream_t; NULL means the default stream) and returns.  It keeps no
+ * state between calls and is reentrant.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * launched; a failed validation returns the status and enqueues nothing.  A
+ * launch error reported by the HIP runtime returns FA_ERR_HIP.  Outputs must
+ * not alias inputs or each other.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or sizes overflow */
+  FA_ERR_STRIDE = 3,      /* stride or alignment rule violated */
+  FA_ERR_DTYPE = 4,       /* unknown input dtype */
+  FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128}, causal != 0, or a non-finite/negative scale */
+  FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
+  FA_ERR_HIP = 7          /* the HIP runtime reported a launch error */
+} fa_status;
+
+typedef enum fa_dtype {
+  FA_BF16 = 0, /* bfloat16 inputs; contractions on bf16 MFMA, fp32 accumulate */
+  FA_FP32 = 1  /* fp32 inputs; contractions on fp32 MFMA */
+} fa_dtype;
+
+typedef struct fa_problem {
+  int64_t B, H, N, d;
+  float scale;      /* tau; a value <= 0 selects 1/sqrt(d) */
+  int32_t causal;   /* must be 0 */
+  int32_t in_dtype; /* an fa_dtype */
+} fa_problem;
+
+typedef struct fa_tensor {
+  void* ptr; /* device pointer */
+  int64_t stride_b, stride_h, stride_n; /* element strides; head dim stride is 1 */
+} fa_tensor;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/*
+ * fa_fwd -- softmax attention forward, [FlashBoB] section 3:
+ *   S = tau Q K^T,  P = softmax(S) row-wise,  O = P V,
+ *   L_i = log sum_j exp(S_ij)   (natural log; the saved row statistic from
+ *                                which P_ij = exp(S_ij - L_i) is rebuilt,
+ *                                [FA2-recompute]).
+ * In:  q, k, v  (in_dtype).
+ * Out: o (fp32, N x d per head), lse (fp32 [B,H,N]).
+ * Online softmax over key tiles ([FA2-triton]); nothing N x N is stored.
+ */
+fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
+                 fa_tensor o, float* lse, void* stream);
+
+/* Workspace bytes fa_bwd needs: the row vector D, B*H*N fp32. */
+size_t fa_bwd_workspace_bytes(const fa_problem* p);
+
+/*
+ * fa_bwd -- first backward at output cotangent dO, [FlashBoB] section 3:
+ *   dP = dO V^T, dV = P^T dO, dS_ij = P_ij (dP_ij - D_i),
+ *   dQ = tau dS K, dK = tau dS^T Q,
+ * with D_i = rowsum(dO * O)_i ([FA2-recompute]), computed by a row-scalar
+ * kernel into the workspace (first B*H*N floats).
+ * In:  q, k, v, dout (in_dtype); o (fp32) and lse (fp32) from fa_fwd.
+ * Out: dq, dk, dv (fp32).  Deterministic: every output block has one writer.
+ */
+fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
+                 fa_tensor o, const float* lse, fa_tensor dout,
+                 fa_tensor dq, fa_tensor dk, fa_tensor dv,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fa_bob needs: D, alpha, E, each B*H*N fp32, in that order. */
+size_t fa_bob_workspace_bytes(const fa_problem* p);
+
+/*
+ * fa_bob -- exact backward-over-backward, [FlashBoB] sections 4.1-4.3 and
+ * appendix D ("Final assembled identities").  With cotangents U_Q, U_K, U_V
+ * on the first-backward outputs dQ, dK, dV, the functional
+ *   Phi = <dQ, U_Q> + <dK, U_K> + <dV, U_V>
+ * is differentiated with respect to Q, K, V and dO (total derivatives: O and
+ * L are functions of Q, K, V):
+ *   F = tau (U_Q K^T + Q U_K^T),  alpha_i = sum_j P_ij F_ij,  C = dO U_V^T,
+ *   d~P = C + F (dP - D) - alpha dP,  E_i = sum_j P_ij d~P_ij,
+ *   d~S = P (d~P - E),  h = F - alpha,
+ *   gq  = tau (d~S K + dS U_K),     gk  = tau (d~S^T Q + dS^T U_Q),
+ *   gv  = (P h)^T dO,               gdo = P U_V + (P h) V.
+ * Schedule ([FlashBoB] section 4.3): a row-scalar kernel writes D; a
+ * row-major pass accumulates the row outputs with the affine corrections of
+ * section 4.2 and writes gq, gdo, alpha, E once per row block; a
+ * column-major pass writes gk, gv once per column block.  No N x N tensor is
+ * written anywhere and no atomics are used, so results are deterministic.
+ * In:  q, k, v, dout, uq, uk, uv (in_dtype); o (fp32), lse (fp32) from fa_fwd.
+ * Out: gq, gk, gv, gdo (fp32).  Workspace: [D | alpha | E], each contiguous
+ *      [B,H,N] fp32 (this layout is part of the ABI).
+ */
+fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
+                 fa_tensor o, const float* lse, fa_tensor dout,
+                 fa_tensor uq, fa_tensor uk, fa_tensor uv,
+                 fa_tensor gq, fa_tensor gk, fa_tensor gv, fa_tensor gdo,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bob_phase -- one kernel of fa_bob, for per-kernel timing and profiling.
+ * Same arguments as fa_bob plus `phase`: 0 launches the row-scalar kernel
+ * (writes D), 1 the row-major pass (reads D; writes gq, gdo, alpha, E), 2 the
+ * column-major pass (reads D, alpha, E; writes gk, gv).  Calling phases 0, 1,
+ * 2 in that order on one stream is exactly fa_bob.  A phase outside 0..2
+ * returns FA_ERR_UNSUPPORTED.
+ */
+fa_status fa_bob_phase(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
+                       fa_tensor o, const float* lse, fa_tensor dout,
+                       fa_tensor uq, fa_tensor uk, fa_tensor uv,
+                       fa_tensor gq, fa_tensor gk, fa_tensor gv, fa_tensor gdo,
+                       void* workspace, size_t workspace_bytes, int32_t phase,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every function declared in include/fa.h.
+Argument validation runs on the host before anything is launched, so the
+error paths below never reach the HIP runtime: every call here returns a
+status before a launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_second_order_fa_amd as fa
+from exact_second_order_fa_amd import FaProblem, FaTensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_second_order_fa_amd import build
+
+        build.build()
+    return fa.load_library()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.SYMBOLS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fa_version() == 10000
+    for code in range(8):
+        s = lib.fa_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_str(99).decode() == "unknown status"
+
+
+def prob(B=1, H=2, N=100, d=64, scale=-1.0, causal=0, dt=fa.FA_BF16):
+    return FaProblem(B, H, N, d, scale, causal, dt)
+
+
+def test_workspace_sizes(lib):
+    p = prob(2, 3, 130, 64)
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == 3 * 2 * 3 * 130 * 4
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 2 * 3 * 130 * 4
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(d=96))) == 0
+    assert lib.fa_bob_workspace_bytes(None) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any launch
+
+
+def t(ptr=FAKE, sb=2 * 100 * 64, sh=100 * 64, sn=64):
+    return FaTensor(ptr, sb, sh, sn)
+
+
+def bob(lib, p, tensors=None, lse=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    ts = tensors or [t() for _ in range(12)]
+    return lib.fa_bob(p if p is None else ctypes.byref(p), ts[0], ts[1], ts[2], ts[3], lse, ts[4], ts[5],
+                      ts[6], ts[7], ts[8], ts[9], ts[10], ts[11], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("p,status", [
+    (None, 1),
+    (prob(B=0), 2),
+    (prob(N=0), 2),
+    (prob(dt=7), 4),
+    (prob(d=96), 5),
+    (prob(d=32), 5),
+    (prob(causal=1), 5),
+    (prob(d=128, dt=fa.FA_FP32), 5),
+    (prob(scale=float("nan")), 5),
+    (prob(scale=float("inf")), 5),
+    (prob(N=(1 << 30) + 1), 2),
+])
+def test_problem_validation(lib, p, status):
+    assert bob(lib, p) == status
+
+
+def test_tensor_validation(lib):
+    p = prob()
+    bad = [t() for _ in range(12)]
+    bad[4] = t(ptr=0)
+    assert bob(lib, p, bad) == 1  # null dout
+    bad = [t() for _ in range(12)]
+    bad[0] = t(ptr=FAKE + 8)
+    assert bob(lib, p, bad) == 3  # misaligned
+    bad = [t() for _ in range(12)]
+    bad[1] = t(sn=32)
+    assert bob(lib, p, bad) == 3  # row stride shorter than d
+    bad = [t() for _ in range(12)]
+    bad[2] = t(sn=68)
+    assert bob(lib, p, bad) == 3  # row stride not a multiple of 16 bytes (bf16)
+    bad = [t() for _ in range(12)]
+    bad[3] = t(sn=66)  # o is fp32: 66 floats is not a multiple of 16 bytes
+    assert bob(lib, p, bad) == 3
+    assert bob(lib, p, lse=0) == 1
+    assert bob(lib, p, lse=FAKE + 2) == 3
+
+
+def test_workspace_validation(lib):
+    p = prob()
+    need = lib.fa_bob_workspace_bytes(ctypes.byref(p))
+    assert bob(lib, p, ws=0) == 6
+    assert bob(lib, p, ws_bytes=need - 4) == 6
+    assert bob(lib, p, ws=FAKE + 4) == 6
+    pb = prob()
+    ts = [t() for _ in range(8)]
+    assert lib.fa_bwd(ctypes.byref(pb), ts[0], ts[1], ts[2], ts[3], FAKE, ts[4], ts[5], ts[6], ts[7],
+                      FAKE, lib.fa_bwd_workspace_bytes(ctypes.byref(pb)) - 1, None) == 6
+
+
+def test_fwd_validation(lib):
+    p = prob(d=80)
+    assert lib.fa_fwd(ctypes.byref(p), t(), t(), t(), t(), FAKE, None) == 5
+    p = prob()
+    assert lib.fa_fwd(ctypes.byref(p), t(), t(), t(ptr=0), t(), FAKE, None) == 1
+    assert lib.fa_fwd(ctypes.byref(p), t(), t(), t(), t(), 0, None) == 1

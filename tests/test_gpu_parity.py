@@ -1,0 +1,120 @@
+"""Parity of the HIP path (through the C ABI) with the float64 CPU oracle.
+
+Tolerance (per output tensor, whole tensor): max |gpu - oracle| / max |oracle|
+<= 2e-2 for bf16 inputs and <= 1e-4 for fp32 inputs.  The same bar is applied
+to the forward (O, L), the first backward (dQ, dK, dV) and the row scalars
+(D, alpha, E) the BoB path writes to its workspace.
+
+Small cases (several tiles and a ragged tail, ragged and degenerate N,
+strided layouts, non power-of-two scales) compare every element with the
+dense oracle.  The full-size workloads are in test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+
+from fa_inputs import make_inputs
+from oracle import bob_dense
+from tests.gpu_helpers import NAMES, host, rel, run_path, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+ALL = ("O", "L", "dQ", "dK", "dV", "D", "alpha", "E", "gQ", "gK", "gV", "gdO")
+
+
+def oracle_heads(f64, scale):
+    B, H = f64["q"].shape[:2]
+    out = {}
+    for b in range(B):
+        for h in range(H):
+            r = bob_dense(*(f64[n][b, h] for n in NAMES), scale)
+            for key in ALL:
+                out.setdefault(key, np.zeros((B, H) + r[key].shape))[b, h] = r[key]
+    return out
+
+
+def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd"):
+    say(f"case B={B} H={H} N={N} d={d} {dtype} seed={seed} scale={scale} layout={layout}")
+    raw, f64 = make_inputs(B, H, N, d, seed, dtype, cot_std=cot, qk_gain=qk)
+    tau = scale if scale is not None else 1.0 / np.sqrt(d)
+    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout)
+    ref = oracle_heads(f64, tau)
+    errs = {k: rel(host(got[k]), ref[k]) for k in ALL}
+    say("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, bad
+    return got
+
+
+def test_tiny_fp32_workload():
+    """B=1, H=1, N=128, d=64, fp32 inputs, seed 0, tolerance 1e-4."""
+    check_case(1, 1, 128, 64, "fp32", 0)
+
+
+@pytest.mark.parametrize("B,H,N,d", [
+    (1, 2, 100, 64),   # one ragged tile
+    (1, 1, 37, 64),    # ragged, smaller than a sub-tile
+    (2, 3, 130, 64),   # several heads, ragged resident block
+    (1, 1, 640, 64),   # ten streamed tiles
+    (1, 2, 300, 128),  # d = 128 (tau not a power of two)
+    (1, 1, 257, 128),
+])
+def test_bf16_shapes(B, H, N, d):
+    check_case(B, H, N, d, "bf16", 100 + N + d)
+
+
+def test_single_key_degenerate():
+    """N = 1: P = 1 and dS = 0 exactly, so dQ, dK, gQ, gK are exactly 0 in the
+    oracle and a relative error is undefined for them.  They are held to the
+    bf16 bar relative to the size of the terms that cancel in them
+    (tau |do| |u_V| |k|-sized products); every other output uses the usual
+    relative bar."""
+    for d in (64, 128):
+        raw, f64 = make_inputs(1, 2, 1, d, 401 + d, "bf16")
+        tau = 1.0 / np.sqrt(d)
+        got = run_path(to_device(raw, "bf16"))
+        ref = oracle_heads(f64, tau)
+        m = {n: np.max(np.abs(f64[n])) for n in NAMES}
+        terms = tau * (m["do"] * (m["uv"] + m["v"]) + m["uq"] * m["k"] + m["q"] * m["uk"]) * max(
+            m["k"], m["uk"], m["q"], m["uq"])
+        for key in ALL:
+            if np.max(np.abs(ref[key])) == 0.0:
+                assert np.max(np.abs(host(got[key]))) <= 2e-2 * terms, key
+            else:
+                assert rel(host(got[key]), ref[key]) <= 2e-2, key
+
+
+@pytest.mark.parametrize("B,H,N", [(1, 1, 257), (2, 1, 70)])
+def test_fp32_shapes(B, H, N):
+    check_case(B, H, N, 64, "fp32", 200 + N)
+
+
+def test_custom_scale_bf16():
+    """A scale that is not a power of two at d = 64 (rho != 1 path)."""
+    check_case(1, 2, 200, 64, "bf16", 301, scale=0.1)
+
+
+def test_custom_scale_fp32():
+    check_case(1, 1, 150, 64, "fp32", 302, scale=0.3)
+
+
+def test_peaked_rows():
+    """Q, K scaled by 2 (peaked softmax rows) and small cotangents."""
+    check_case(1, 2, 512, 64, "bf16", 303, qk=2.0, cot=0.1)
+    check_case(1, 1, 256, 128, "bf16", 304, qk=2.0, cot=0.1)
+
+
+def test_strided_layout():
+    """Inputs and outputs stored [B, N, H, d] (non-contiguous head stride)."""
+    check_case(2, 3, 150, 64, "bf16", 305, layout="bnhd")
+    check_case(1, 2, 90, 128, "bf16", 306, layout="bnhd")
+
+
+def test_deterministic():
+    """No atomics: two runs are bitwise identical."""
+    raw, _ = make_inputs(1, 2, 333, 64, 307, "bf16")
+    t = to_device(raw, "bf16")
+    a = run_path(t)
+    b = run_path(t)
+    for key in ("O", "L", "dQ", "dK", "dV", "gQ", "gK", "gV", "gdO", "alpha", "E"):
+        assert bool((a[key] == b[key]).all()), key

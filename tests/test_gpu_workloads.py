@@ -1,0 +1,136 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (the same entry points, contiguous [B, H, N, d] tensors).
+
+* tiny (B=1,H=1,N=128,d=64, fp32): every element vs the dense oracle, 1e-4.
+* mid (B=2,H=8,N=4096,d=64, bf16): every element of every output vs the
+  streaming float64 oracle run in-test, 2e-2.
+* hd128 / long / max (N = 16K, 64K, 262K): the oracle cannot redo the full
+  O(N^2 d) sweeps inside a test, so
+    - row-owned outputs (gQ, gdO, alpha, E, and O, L, D, dQ) are compared on
+      seeded sample rows, computed one by one by the oracle in-test;
+    - column-owned outputs (gK, gV, dK, dV) are compared on seeded sample
+      columns against values stored in tests/golden/<name>_cols.npz, written
+      by tests/golden/make_golden.py, which calls only the oracle;
+    - two properties that hold at any size are checked on the whole output:
+      sum_j gK_j = 0 and sum_j gV_j = 0 per head (rows of dS and d~S sum to 0).
+* max also checks that the BoB call allocates no device memory and that the
+  whole pipeline stays far below one N x N buffer (128 GiB in bf16).
+"""
+import os
+
+import numpy as np
+import pytest
+
+from fa_inputs import WORKLOADS, workload_inputs
+from oracle import bob_dense, bob_streaming, row_pass
+from tests.gpu_helpers import NAMES, host, oracle_threads, rel, run_path, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+
+
+def test_tiny_workload_full():
+    w = WORKLOADS["tiny"]
+    say("workload tiny")
+    raw, f64 = workload_inputs(w)
+    got = run_path(to_device(raw, w.dtype))
+    ref = bob_dense(*(f64[n][0, 0] for n in NAMES), w.scale)
+    for key in ("O", "L", "dQ", "dK", "dV", "D", "alpha", "E", "gQ", "gK", "gV", "gdO"):
+        e = rel(host(got[key])[0, 0], ref[key])
+        say(f"  {key} {e:.2e}")
+        assert e <= TOL["fp32"], key
+
+
+def test_mid_workload_full():
+    w = WORKLOADS["mid"]
+    say("workload mid: GPU path")
+    raw, f64 = workload_inputs(w)
+    got = run_path(to_device(raw, w.dtype))
+    say("workload mid: streaming oracle")
+    ref = bob_streaming(*(f64[n] for n in NAMES), w.scale, threads=oracle_threads())
+    for key in ("O", "L", "dQ", "dK", "dV", "D", "alpha", "E", "gQ", "gK", "gV", "gdO"):
+        e = rel(host(got[key]), ref[key])
+        say(f"  {key} {e:.2e}")
+        assert e <= TOL["bf16"], key
+
+
+def _sampled(name):
+    w = WORKLOADS[name]
+    path = os.path.join(GOLDEN, f"{name}_cols.npz")
+    g = np.load(path, allow_pickle=False)
+    say(f"workload {name}: GPU path")
+    raw, f64 = workload_inputs(w)
+    got = run_path(to_device(raw, w.dtype))
+    del raw
+    heads = sorted({tuple(x) for x in g["heads"].tolist()})
+    # column-owned outputs vs stored oracle values
+    for key in ("gK", "gV", "dK", "dV"):
+        vals = np.stack([host(got[key][b, h, c]) for (b, h), c in zip(g["heads"], g["cols"])])
+        e = rel(vals, g[key])
+        say(f"  {key} sampled columns {e:.2e}")
+        assert e <= TOL[w.dtype], key
+    # stored row scalars
+    for key in ("L", "D", "alpha", "E"):
+        vals = np.array([float(got[key][b, h, r]) for b, h, r in g["state_rows"]])
+        e = rel(vals, g[key])
+        say(f"  {key} stored rows {e:.2e}")
+        assert e <= TOL[w.dtype], key
+    # row-owned outputs computed one by one in-test
+    rng = np.random.default_rng(5000 + w.seed)
+    for (b, h) in heads:
+        rows = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, size=22, replace=False)]))
+        say(f"  oracle rows head ({b},{h})")
+        r = row_pass(*(f64[n][b, h] for n in NAMES), w.scale, rows=rows, outputs="all",
+                     strip=4, threads=oracle_threads())
+        for key in ("gQ", "gdO", "dQ", "O", "L", "D", "alpha", "E"):
+            e = rel(host(got[key][b, h][rows]), r[key])
+            say(f"  {key} head ({b},{h}) sampled rows {e:.2e}")
+            assert e <= TOL[w.dtype], (key, b, h)
+    # properties of the whole column-owned outputs
+    for key in ("gK", "gV"):
+        x = got[key].double()
+        s = x.sum(dim=2).abs().amax().item()
+        bound = 2e-2 * np.sqrt(w.N) * x.abs().amax().item()
+        say(f"  |sum_j {key}_j| = {s:.3e} (bound {bound:.3e})")
+        assert s <= bound, key
+    return w, got
+
+
+def test_hd128_workload_sampled():
+    _sampled("hd128")
+
+
+def test_long_workload_sampled():
+    _sampled("long")
+
+
+def test_max_workload_sampled_and_memory():
+    import torch
+
+    import exact_second_order_fa_amd as fa
+
+    w, got = _sampled("max")
+    del got
+    torch.cuda.empty_cache()
+    g = torch.Generator(device="cuda").manual_seed(4)
+    shape = (w.B, w.H, w.N, w.d)
+    t = {n: torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16) for n in NAMES}
+    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"])
+    outs = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(4)]
+    ws = torch.empty(fa.bob_workspace_bytes(*shape) // 4, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"],
+              gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3], ws=ws)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    peak = torch.cuda.max_memory_allocated()
+    say(f"  memory: device free delta {free0 - free1} B, torch peak {peak / 2**20:.0f} MiB, "
+        f"resident {base / 2**20:.0f} MiB")
+    assert free0 - free1 <= 4 << 20          # the library allocates nothing
+    assert peak == base                      # no allocation during the call
+    assert peak < 2 << 30                    # an N x N bf16 buffer would be 128 GiB
