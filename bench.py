@@ -167,6 +167,9 @@ def main():
     ap.add_argument("--sweep", default="hd128,long,max", help="comma list of extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (three times), the reference kernel "
+                         "for scaling the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -175,6 +178,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18  # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}), flush=True)
+        return
 
     from fa_inputs import WORKLOADS
 
