@@ -5,6 +5,7 @@
 
 #include "fa.h"
 #include "fa_kernels.hip"
+#include "fa_bob.hip"
 
 namespace {
 
@@ -64,6 +65,8 @@ fa_status check_tensor(const Ctx& c, const fa_tensor& t, size_t esize) {
   const int64_t vec = 16 / (int64_t)esize;
   if (t.stride_n < c.d || t.stride_h < 0 || t.stride_b < 0) return FA_ERR_STRIDE;
   if (t.stride_n % vec || t.stride_h % vec || t.stride_b % vec) return FA_ERR_STRIDE;
+  // Tile copies address a few rows with 32-bit byte offsets.
+  if (t.stride_n > (int64_t(1) << 26)) return FA_ERR_STRIDE;
   return FA_OK;
 }
 
@@ -142,9 +145,13 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
 template <typename T, int D, bool RHO1>
 void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
   if (phase < 0 || phase == 0) launch_rowscalar<T, D>(c, a, st);
-  if (phase < 0 || phase == 1)
-    hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads),
-                       0, st, a);
+  if (phase < 0 || phase == 1) {
+    if constexpr (sizeof(T) == 2 && D == 64)
+      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
+                         dim3(fa::kThreads), 0, st, a);
+  }
   if (phase < 0 || phase == 2)
     hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads),
                        0, st, a);

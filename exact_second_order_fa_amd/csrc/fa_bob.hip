@@ -1,0 +1,248 @@
+// fa_bob.hip -- bf16 backward-over-backward passes for gfx950 with LDS DMA
+// staging and transposing operand reads (fa_lds.h).
+//
+// Source: [FlashBoB] "FlashBoB: I/O-Efficient Exact Backward-over-Backward
+// for Softmax Attention", section 4.2 (affine fusion, Proposition 4.1 and the
+// corrections (8)), section 4.3 (Algorithm 1, two passes), appendix D (final
+// assembled identities).
+//
+// Work split: one workgroup = 4 waves = 128 resident rows (32 per wave, the
+// N index of v_mfma_f32_32x32x16_bf16); the other side is streamed through
+// LDS in tiles of TS rows, double buffered, filled by DMA.  Inside a tile the
+// 32-row sub-tiles are software pipelined: while the elementwise work of
+// sub-tile s runs on the VALU, the MFMA pipe computes the scores of s + 1 and
+// the accumulations of s - 1.
+#include "fa_lds.h"
+
+namespace fa {
+
+// Bias rows of the score chains: 0 for streamed rows < N, -inf past N (so
+// that exp2 gives P = 0 there), for the tile starting at row0.
+template <int TS>
+__device__ inline void fill_bias(float* b, int row0, int N) {
+  for (int x = threadIdx.x; x < TS; x += kThreads) b[x] = (row0 + x < N) ? 0.0f : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core steps as inline assembly, so that the register class of every
+// operand is fixed: score chains in VGPRs (the VALU consumes them), the
+// output accumulators in AGPRs for the whole kernel, resident operands in
+// AGPRs.  The wait states the hardware needs around v_mfma_f32_32x32x16_bf16
+// (the same counts the compiler inserts for the builtin on gfx950) are
+// explicit:
+//   * a VALU write of an operand -> the MFMA reading it: 2 (s_nop 1 in front
+//     of every MFMA whose B operand the VALU produced);
+//   * an MFMA result -> a VALU or memory read of it: 12 (mfma_fence());
+//   * an MFMA reading a VGPR as C -> a VALU write of it: 7 (C is always the
+//     tied destination here, so the fence above covers it);
+//   * back-to-back accumulation into the same registers needs none.
+
+// d = a * b (a chain start; C = 0).
+__device__ inline f32x16 mfma_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+// d += a * b, d in VGPRs, b resident in AGPRs.
+__device__ inline void mfma_v(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// acc += a * b, acc in AGPRs, b produced by the VALU.
+__device__ inline void mfma_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Results of the chains above may be read by the VALU after this.
+__device__ inline void mfma_fence(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+template <int NDB>
+__device__ inline void acc_fence(f32x16 (&a)[NDB], f32x16 (&b)[NDB], f32x16 (&c)[NDB], f32x16 (&d)[NDB]) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[db]), "+a"(b[db]), "+a"(c[db]), "+a"(d[db]));
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1 (row-major).  Resident per wave: query rows i with q_i, u_Q,i
+// (scaled by pow2), do_i, L_i, D_i.  Streamed: K, V, U_K, U_V.  Per 32 x 32
+// sub-tile (streamed index j on M):
+//   S^T = K Q^T,  F^T = K U_Q^T + U_K Q^T,  dP^T = V dO^T,  C^T = U_V dO^T,
+//   P = exp(tau S - L),  dPD = dP - D,  P~ = C + F dPD  (d~P before the
+//   alpha correction), and the alpha-free accumulators of Proposition 4.1:
+//     alpha += sum_j P F            E° += sum_j P P~
+//     G     += P U_V + (P F) V      (d~(dO) before the correction)
+//     Om    += (P P~) K + dS U_K    with dS = P dPD
+//     R'    += dS K                 Bk += P K
+// Epilogue (the corrections (8); R = R' + D Bk, so alpha R + E Bk =
+// alpha R' + E° Bk):
+//     E = E° - alpha D,  gdo = G - alpha o,  gq = tau (Om - alpha R' - E° Bk).
+//
+// Schedule of one tile (NSUB sub-tiles): scores(0); then for each sub-tile s
+// the elementwise work of s interleaved with the accumulations of s - 1, and
+// the scores of s + 1.
+template <int D, int TS, bool RHO1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_dma_kernel(Args a) {
+  typedef SwTile<D, TS> W;
+  constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
+  constexpr int NSLICE = 2 * NDB;  // (d-block, k-step) pairs of one accumulation
+  constexpr int STAGE = 4 * W::BYTES;
+  static_assert(NSLICE == 4 || NSLICE == 8, "slices");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float kbias[2][TS];  // [0]: all valid, [1]: last tile
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<bf16> q = head_of<bf16>(a.q, wk.b, wk.h), uq = head_of<bf16>(a.uq, wk.b, wk.h),
+                      dout = head_of<bf16>(a.dout, wk.b, wk.h);
+  HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, wk.b, wk.h), head_of<bf16>(a.v, wk.b, wk.h),
+                          head_of<bf16>(a.uk, wk.b, wk.h), head_of<bf16>(a.uv, wk.b, wk.h)};
+  const int nt = (N + TS - 1) / TS;
+
+  // Start the first tile's copy before anything else.
+  Dma<D, TS, 4> dma;
+  dma.init(src);
+  dma.copy(0, N, lds);
+  fill_bias<TS>(kbias[0], 0, 1 << 30);
+  fill_bias<TS>(kbias[1], (nt - 1) * TS, N);
+
+  bf16x8 qf[NKS], uqf[NKS], df[NKS];
+  load_resident<bf16, D>(qf, q.p, q.sn, row, N, a.pow2);
+  load_resident<bf16, D>(uqf, uq.p, uq.sn, row, N, a.pow2);
+  load_resident<bf16, D>(df, dout.p, dout.sn, row, N, 1.0f);
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float Li = row < N ? a.lse[rv + row] : 0.0f;
+  const float Di = row < N ? a.D[rv + row] : 0.0f;
+  const float nl2 = -Li * kLog2e;
+
+  Reader<D, TS> rd;
+  rd.init();
+
+  f32x16 ag[NDB], aom[NDB], ar[NDB], abk[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ag[db] = aom[db] = ar[db] = abk[db] = zero16();
+    asm volatile("" : "+a"(ag[db]), "+a"(aom[db]), "+a"(ar[db]), "+a"(abk[db]));
+  }
+  float alpha_p = 0.0f, eo_p = 0.0f;
+  // No load of the compiler's own may be outstanding inside the loop.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  for (int t = 0; t < nt; ++t) {
+    const char* tk = lds + (t & 1) * STAGE;
+    const char* tv = tk + W::BYTES;
+    const char* tuk = tk + 2 * W::BYTES;
+    const char* tuv = tk + 3 * W::BYTES;
+    const float* kb = kbias[t == nt - 1 ? 1 : 0];
+    // This wave's copies of tile t are done; the barrier makes every wave's
+    // copies visible and guarantees that no wave still reads `next`.
+    dma_wait();
+    __syncthreads();
+    if (t + 1 < nt) dma.copy((t + 1) * TS, N, lds + ((t + 1) & 1) * STAGE);
+
+    auto scores = [&](int sub, f32x16& s, f32x16& f, f32x16& dp, f32x16& c) {
+      s = row_init<TS>(kb, sub);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 xk = rd_row<D, TS>(tk, rd, sub, ks);
+        const bf16x8 xuk = rd_row<D, TS>(tuk, rd, sub, ks);
+        const bf16x8 xv = rd_row<D, TS>(tv, rd, sub, ks);
+        const bf16x8 xuv = rd_row<D, TS>(tuv, rd, sub, ks);
+        mfma_v(s, xk, qf[ks]);
+        if (ks == 0) {
+          f = mfma_first(xk, uqf[0]);
+          dp = mfma_first(xv, df[0]);
+          c = mfma_first(xuv, df[0]);
+        } else {
+          mfma_v(f, xk, uqf[ks]);
+          mfma_v(dp, xv, df[ks]);
+          mfma_v(c, xuv, df[ks]);
+        }
+        mfma_v(f, xuk, qf[ks]);
+      }
+    };
+    // One (d-block, k-step) slice of the accumulations of sub-tile `sub`.
+    auto acc_slice = [&](int sub, int sl, const Chain<bf16>& cp, const Chain<bf16>& cpf,
+                         const Chain<bf16>& cpt, const Chain<bf16>& cds) {
+      const int db = sl >> 1, s2 = sl & 1;
+      const bf16x8 xuv = rd_tr<D, TS>(tuv, rd, sub, db, s2);
+      const bf16x8 xv = rd_tr<D, TS>(tv, rd, sub, db, s2);
+      const bf16x8 xk = rd_tr<D, TS>(tk, rd, sub, db, s2);
+      const bf16x8 xuk = rd_tr<D, TS>(tuk, rd, sub, db, s2);
+      mfma_acc(ag[db], xuv, cp.f[s2]);
+      mfma_acc(ag[db], xv, cpf.f[s2]);
+      mfma_acc(aom[db], xk, cpt.f[s2]);
+      mfma_acc(aom[db], xuk, cds.f[s2]);
+      mfma_acc(ar[db], xk, cds.f[s2]);
+      mfma_acc(abk[db], xk, cp.f[s2]);
+    };
+
+    f32x16 s, f, dp, c;
+    scores(0, s, f, dp, c);
+    Chain<bf16> pp, ppf, ppt, pds;  // chains of the previous sub-tile
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      mfma_fence(s, f, dp, c);
+      Chain<bf16> cp, cpf, cpt, cds;
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * part + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
+          const float F = RHO1 ? f[idx] : f[idx] * a.rho;
+          const float dpd = dp[idx] - Di;
+          const float t0 = fmaf(F, dpd, c[idx]);
+          const float pf = p * F, pt = p * t0;
+          alpha_p += pf;
+          eo_p += pt;
+          cp.f[idx >> 3][idx & 7] = (bf16)p;
+          cpf.f[idx >> 3][idx & 7] = (bf16)pf;
+          cpt.f[idx >> 3][idx & 7] = (bf16)pt;
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
+        }
+        if (sub > 0) {
+#pragma unroll
+          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl) acc_slice(sub - 1, sl, pp, ppf, ppt, pds);
+        }
+      }
+      pp = cp;
+      ppf = cpf;
+      ppt = cpt;
+      pds = cds;
+      if (sub + 1 < NSUB) scores(sub + 1, s, f, dp, c);
+    }
+#pragma unroll
+    for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl, pp, ppf, ppt, pds);
+  }
+
+  acc_fence<NDB>(ag, aom, ar, abk);
+  const float alpha = half_sum(alpha_p);
+  const float eo = half_sum(eo_p);
+  if (row < N && hh == 0) {
+    a.alpha[rv + row] = alpha;
+    a.E[rv + row] = eo - alpha * Di;
+  }
+  const HeadPtr<float> o = head_of<float>(a.o, wk.b, wk.h);
+  float* gq = head_out(a.r0, wk.b, wk.h);
+  float* gdo = head_out(a.r3, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    float ov[16];
+    if (row < N) {
+      const float* orow = o.p + (int64_t)row * o.sn + db * 32 + 4 * hh;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(orow + 8 * b4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[4 * b4 + e] = x[e];
+      }
+    }
+    store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx] - alpha * ov[idx]; });
+    store_out(gq, a.r0.sn, row, N, db,
+              [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eo * abk[db][idx]); });
+  }
+}
+
+}  // namespace fa

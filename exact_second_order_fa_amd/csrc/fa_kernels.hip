@@ -64,6 +64,50 @@ __device__ inline Work work_item(const Args& a) {
   return r;
 }
 
+// Row scalars of a streamed tile, staged into LDS next to the operand tiles.
+// NS scalars per streamed row; Fn maps (global row) -> values and Pad gives
+// the values of rows past N.  The scalars enter the score chains as MFMA
+// accumulator initial values, and a -inf there is what masks a ragged tile
+// (exp2(-inf) = 0), so no per-element select is needed in the inner loop.
+template <int TS, int NS>
+struct ScalarStager {
+  float v[NS];
+  bool active;
+  template <typename Fn, typename Pad>
+  __device__ inline void load(int row0, int N, Fn fn, Pad pad) {
+    active = threadIdx.x < TS;
+    if (active) {
+      const int row = row0 + threadIdx.x;
+      if (row < N) {
+        fn(row, v);
+      } else {
+        pad(v);
+      }
+    }
+  }
+  __device__ inline void store(float* lds) const {
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < NS; ++e) lds[e * TS + threadIdx.x] = v[e];
+    }
+  }
+};
+
+// Chain-initial value of a score-shaped accumulator from a staged per-row
+// scalar array: element idx gets sc[sub*32 + acc_pos(idx, hh)].
+template <int TS>
+__device__ inline f32x16 row_init(const float* sc, int sub) {
+  const int hh = lane_id() >> 5;
+  f32x16 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(sc + sub * 32 + sig(8 * b + 4 * hh));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * b + e] = x[e];
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Row-scalar preprocessing: D_i = sum_c dO_ic O_ic ([FA2-recompute]; the
 // first backward's D_i = sum_j P_ij dP_ij).  HBM-bound: D/8 lanes per row,
@@ -120,6 +164,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   typedef Stage<T, D, TS> S;
   constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
   __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
+  __shared__ __attribute__((aligned(16))) float kbias[2][TS];
 
   const Work wk = work_item(a);
   const int N = a.N;
@@ -138,24 +183,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 2> st;
   const int nt = (N + TS - 1) / TS;
+  ScalarStager<TS, 1> ks;
+  auto kvalid = [](int, float* o) { o[0] = 0.0f; };
+  auto kpad = [](float* o) { o[0] = -INFINITY; };
   st.load(src, 0, N);
+  ks.load(0, N, kvalid, kpad);
   st.store(lds[0]);
+  ks.store(kbias[0]);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) st.load(src, (t + 1) * TS, N);
+    if (t + 1 < nt) {
+      st.load(src, (t + 1) * TS, N);
+      ks.load((t + 1) * TS, N, kvalid, kpad);
+    }
+    const float* kb = kbias[t & 1];
     const T* kr = lds[t & 1];
     const T* vt = lds[t & 1] + S::ELEMS + S::ROW_ELEMS;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, zero16());
-      const int j0 = t * TS + sub * 32;
-      const bool full = j0 + 32 <= N;
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, row_init<TS>(kb, sub));
       float z[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         z[idx] = s[idx] * a.c1;
-        if (!full && j0 + acc_pos(idx, hh) >= N) z[idx] = -INFINITY;
         mx = fmaxf(mx, z[idx]);
       }
       mx = half_max(mx);
@@ -181,7 +232,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int s2 = 0; s2 < KS32; ++s2) acc[db] = E::mma(tr_frag<T, D, TS>(vt, db, sub, s2), cp.f[s2], acc[db]);
       }
     }
-    if (t + 1 < nt) st.store(lds[(t + 1) & 1]);
+    if (t + 1 < nt) {
+      st.store(lds[(t + 1) & 1]);
+      ks.store(kbias[(t + 1) & 1]);
+    }
     __syncthreads();
   }
   const float lt = half_sum(lsum);
@@ -201,6 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   typedef Stage<T, D, TS> S;
   constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
   __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
+  __shared__ __attribute__((aligned(16))) float kbias[2][TS];
 
   const Work wk = work_item(a);
   const int N = a.N;
@@ -223,25 +278,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 2> st;
   const int nt = (N + TS - 1) / TS;
+  ScalarStager<TS, 1> ks;
+  auto kvalid = [](int, float* o) { o[0] = 0.0f; };
+  auto kpad = [](float* o) { o[0] = -INFINITY; };
   st.load(src, 0, N);
+  ks.load(0, N, kvalid, kpad);
   st.store(lds[0]);
+  ks.store(kbias[0]);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) st.load(src, (t + 1) * TS, N);
+    if (t + 1 < nt) {
+      st.load(src, (t + 1) * TS, N);
+      ks.load((t + 1) * TS, N, kvalid, kpad);
+    }
+    const float* kb = kbias[t & 1];
     const T* kr = lds[t & 1];
     const T* kt = kr + S::ROW_ELEMS;
     const T* vr = kr + S::ELEMS;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, zero16());
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, row_init<TS>(kb, sub));
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
-      const int j0 = t * TS + sub * 32;
-      const bool full = j0 + 32 <= N;
       float ds[16];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
-        if (!full && j0 + acc_pos(idx, hh) >= N) p = 0.0f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
         ds[idx] = p * (dp[idx] - Di);
       }
       Chain<T> cds;
@@ -251,54 +312,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int s2 = 0; s2 < KS32; ++s2) acc[db] = E::mma(tr_frag<T, D, TS>(kt, db, sub, s2), cds.f[s2], acc[db]);
     }
-    if (t + 1 < nt) st.store(lds[(t + 1) & 1]);
+    if (t + 1 < nt) {
+      st.store(lds[(t + 1) & 1]);
+      ks.store(kbias[(t + 1) & 1]);
+    }
     __syncthreads();
   }
   float* dq = head_out(a.r0, wk.b, wk.h);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) store_out(dq, a.r0.sn, row, N, db, [&](int idx) { return a.tau * acc[db][idx]; });
-}
-
-// Row scalars of a streamed tile, staged into LDS next to the operand tiles.
-// NS scalars per streamed row; Fn maps (global row) -> values.
-template <int TS, int NS>
-struct ScalarStager {
-  float v[NS];
-  bool active;
-  template <typename Fn>
-  __device__ inline void load(int row0, int N, Fn fn) {
-    active = threadIdx.x < TS;
-    if (active) {
-      const int row = row0 + threadIdx.x;
-      if (row < N) {
-        fn(row, v);
-      } else {
-#pragma unroll
-        for (int e = 0; e < NS; ++e) v[e] = 0.0f;
-      }
-    }
-  }
-  __device__ inline void store(float* lds) const {
-    if (active) {
-#pragma unroll
-      for (int e = 0; e < NS; ++e) lds[e * TS + threadIdx.x] = v[e];
-    }
-  }
-};
-
-// Chain-initial value of a score-shaped accumulator from a staged per-row
-// scalar array: element idx gets sc[sub*32 + acc_pos(idx, hh)].
-template <int TS>
-__device__ inline f32x16 row_init(const float* sc, int sub) {
-  const int hh = lane_id() >> 5;
-  f32x16 r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(sc + sub * 32 + sig(8 * b + 4 * hh));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[4 * b + e] = x[e];
-  }
-  return r;
 }
 
 // First backward, column side: dV = P^T dO, dK = tau dS^T Q
@@ -328,6 +350,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     o[0] = -a.lse[rv + row] * irho;
     o[1] = -a.D[rv + row];
   };
+  auto pad = [](float* o) {
+    o[0] = -INFINITY;
+    o[1] = 0.0f;
+  };
 
   f32x16 ak[NDB], av[NDB];
 #pragma unroll
@@ -337,14 +363,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   ScalarStager<TS, 2> ss;
   const int nt = (N + TS - 1) / TS;
   st.load(src, 0, N);
-  ss.load(0, N, scal);
+  ss.load(0, N, scal, pad);
   st.store(lds[0]);
   ss.store(scl[0]);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     if (t + 1 < nt) {
       st.load(src, (t + 1) * TS, N);
-      ss.load((t + 1) * TS, N, scal);
+      ss.load((t + 1) * TS, N, scal, pad);
     }
     const T* qr = lds[t & 1];
     const T* qt = qr + S::ROW_ELEMS;
@@ -355,13 +381,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, row_init<TS>(sc, sub));
       const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
-      const int i0 = t * TS + sub * 32;
-      const bool full = i0 + 32 <= N;
       float p[16], ds[16];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float pp = __builtin_amdgcn_exp2f(s[idx] * a.c1);
-        if (!full && i0 + acc_pos(idx, hh) >= N) pp = 0.0f;
+        const float pp = __builtin_amdgcn_exp2f(s[idx] * a.c1);
         p[idx] = pp;
         ds[idx] = pp * dp[idx];
       }
@@ -413,6 +436,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   typedef Stage<T, D, TS> S;
   constexpr int NKS = D / E::KS, NDB = D / 32, NSUB = TS / 32, KS32 = ksteps32<T>();
   __shared__ __attribute__((aligned(16))) T lds[2][4 * S::ELEMS];
+  __shared__ __attribute__((aligned(16))) float kbias[2][TS];
 
   const Work wk = work_item(a);
   const int N = a.N;
@@ -439,11 +463,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 4> st;
   const int nt = (N + TS - 1) / TS;
+  ScalarStager<TS, 1> ks;
+  auto kvalid = [](int, float* o) { o[0] = 0.0f; };
+  auto kpad = [](float* o) { o[0] = -INFINITY; };
   st.load(src, 0, N);
+  ks.load(0, N, kvalid, kpad);
   st.store(lds[0]);
+  ks.store(kbias[0]);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) st.load(src, (t + 1) * TS, N);
+    if (t + 1 < nt) {
+      st.load(src, (t + 1) * TS, N);
+      ks.load((t + 1) * TS, N, kvalid, kpad);
+    }
+    const float* kb = kbias[t & 1];
     const T* kr = lds[t & 1];
     const T* kt = kr + S::ROW_ELEMS;
     const T* vr = kr + S::ELEMS;
@@ -454,18 +487,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* uvt = uvr + S::ROW_ELEMS;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, zero16());
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, row_init<TS>(kb, sub));
       f32x16 f = mm_row<T, D, TS>(kr, sub, uqf, zero16());
       f = mm_row<T, D, TS>(ukr, sub, qf, f);
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
       const f32x16 c = mm_row<T, D, TS>(uvr, sub, df, zero16());
-      const int j0 = t * TS + sub * 32;
-      const bool full = j0 + 32 <= N;
       float P[16], PF[16], PT[16], DS[16];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
-        if (!full && j0 + acc_pos(idx, hh) >= N) p = 0.0f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
         const float F = RHO1 ? f[idx] : f[idx] * a.rho;
         const float dpd = dp[idx] - Di;
         const float t0 = fmaf(F, dpd, c[idx]);
@@ -497,7 +527,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           abk[db] = E::mma(xk, cp.f[s2], abk[db]);
         }
     }
-    if (t + 1 < nt) st.store(lds[(t + 1) & 1]);
+    if (t + 1 < nt) {
+      st.store(lds[(t + 1) & 1]);
+      ks.store(kbias[(t + 1) & 1]);
+    }
     __syncthreads();
   }
 
@@ -569,6 +602,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     o[2] = -al * irho;
     o[3] = -fmaf(al, Dd, Ee);
   };
+  auto pad = [](float* o) {
+    o[0] = -INFINITY;
+    o[1] = o[2] = o[3] = 0.0f;
+  };
 
   f32x16 ak[NDB], av[NDB];
 #pragma unroll
@@ -578,14 +615,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   ScalarStager<TS, 4> ss;
   const int nt = (N + TS - 1) / TS;
   st.load(src, 0, N);
-  ss.load(0, N, scal);
+  ss.load(0, N, scal, pad);
   st.store(lds[0]);
   ss.store(scl[0]);
   __syncthreads();
   for (int t = 0; t < nt; ++t) {
     if (t + 1 < nt) {
       st.load(src, (t + 1) * TS, N);
-      ss.load((t + 1) * TS, N, scal);
+      ss.load((t + 1) * TS, N, scal, pad);
     }
     const T* qr = lds[t & 1];
     const T* qt = qr + S::ROW_ELEMS;
@@ -601,13 +638,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       f = mm_row<T, D, TS>(qr, sub, ukf, f);
       const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
       const f32x16 c = mm_row<T, D, TS>(dr, sub, uvf, row_init<TS>(sc + 3 * TS, sub));
-      const int i0 = t * TS + sub * 32;
-      const bool full = i0 + 32 <= N;
       float DT[16], DS[16], W[16];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
-        float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
-        if (!full && i0 + acc_pos(idx, hh) >= N) p = 0.0f;
+        const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
         const float h = RHO1 ? f[idx] : f[idx] * a.rho;
         const float x = fmaf(h, dp[idx], c[idx]);
         DT[idx] = p * x;

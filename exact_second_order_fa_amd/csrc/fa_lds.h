@@ -1,0 +1,173 @@
+// fa_lds.h -- LDS staging of streamed bf16 tiles for the gfx950 BoB passes.
+//
+//   * Tiles are copied HBM -> LDS with global_load_lds_dwordx4: every lane
+//     moves one 16-byte granule and the wave's 64 granules land contiguously
+//     at the LDS address the instruction names, so no VGPR holds tile data.
+//   * A tile is TS rows of D bf16 (G = D/8 granules per row) with no padding;
+//     granule q of row j sits at position q ^ swz(j) of the row, which keeps
+//     both read patterns below free of LDS bank conflicts.  The swizzle is
+//     applied on the HBM side: the lane that fills LDS position p fetches the
+//     granule that belongs there.
+//   * Products that contract over d read their A operand (32 streamed rows x
+//     8 consecutive d per lane) with ds_read_b128.
+//   * Products that contract over the streamed index need the transposed
+//     operand (32 d-columns x 8 consecutive streamed rows per lane).  It is
+//     read from the same row-major tile with two ds_read_b64_tr_b16: within
+//     each group of 16 lanes, lane r names an 8-byte piece of row r of a 16 x 4
+//     block and receives element (r % 4) of the pieces named by lanes
+//     4k + r / 4, k = 0..3.
+#pragma once
+
+#include "fa_tile.h"
+
+namespace fa {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Position of granule q inside row j is q ^ swz(j).  Rows 0-3 and 8-11 (the
+// eight rows one ds_read_b128 phase touches after the sig() row permutation)
+// get eight different positions.
+__host__ __device__ constexpr int swz(int j) { return (j + 4 * (j >> 3)) & 7; }
+
+template <int D, int TS>
+struct SwTile {
+  static constexpr int G = D / 8;             // granules per row
+  static constexpr int BYTES = TS * D * 2;    // bytes per tensor tile
+  static constexpr int BLOCKS = TS * G / 64;  // wave-wide DMA copies per tensor tile
+  static_assert((TS * G) % 64 == 0, "a tile must be a whole number of wave copies");
+  static_assert(64 % G == 0, "a wave copy must cover whole rows");
+  static constexpr int ROWS_PER_BLOCK = 64 / G;
+
+  // Byte offset of (row j, granule q).
+  __host__ __device__ static constexpr int off(int j, int q) { return (j * G + (q ^ swz(j))) * 16; }
+};
+
+// One wave-wide HBM -> LDS copy: lane i moves 16 bytes to lds_base + 16 i.
+// Issued as inline assembly so that the compiler does not treat the
+// in-flight copy as a pending write to every LDS location (it would otherwise
+// wait for the copy before the first LDS read of the current tile); the
+// kernels await completion explicitly with dma_wait() before the barrier that
+// publishes a tile.  M0 holds the LDS base for the instruction.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Source = uniform 64-bit base + per-lane 32-bit byte offset.
+__device__ inline void dma16_so(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+// Source = per-lane 64-bit address.
+__device__ inline void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until every copy this wave issued has landed in LDS.
+__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// HBM -> LDS copies of rows [row0, row0 + TS) of NT streamed tensors of one
+// head into NT consecutive tiles.  Wave w copies blocks w, w + NW, ... of
+// every tensor (a block = 64 granules = ROWS_PER_BLOCK rows).  Rows at or
+// past N are read from row N - 1 instead (in bounds; the caller masks their
+// scores to P = 0).
+template <int D, int TS, int NT>
+struct Dma {
+  typedef SwTile<D, TS> W;
+  static constexpr int NW = kThreads / 64;
+  static constexpr int RPB = W::ROWS_PER_BLOCK;
+  static constexpr int PER_WAVE = W::BLOCKS / NW;
+  static_assert(W::BLOCKS % NW == 0, "blocks per tensor must split evenly over the waves");
+  // The swizzle of a row then depends only on the lane and the wave.
+  static_assert((NW * RPB) % 16 == 0, "block stride must keep the row swizzle");
+
+  const char* base[NT];  // head base pointers (uniform)
+  int64_t rs[NT];        // row strides in bytes (uniform)
+  uint32_t off[NT];      // per-lane byte offset inside a block: jl * rs + 16 q
+  int jl, wave;
+
+  __device__ inline void init(const HeadPtr<bf16>* src) {
+    const int lane = lane_id();
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    jl = lane / W::G;
+    const int q = (lane % W::G) ^ swz(wave * RPB + jl);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      base[t] = reinterpret_cast<const char*>(src[t].p);
+      rs[t] = src[t].sn * 2;
+      off[t] = (uint32_t)(jl * (int)rs[t] + 16 * q);
+    }
+  }
+
+  __device__ inline void copy(int row0, int N, const char* dst) const {
+    const uint32_t lbase = lds_addr(dst);
+    const int lane = lane_id();
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int b = i * NW + wave;
+        const int r0 = row0 + b * RPB;
+        const uint32_t lds = lbase + t * W::BYTES + b * 1024;
+        if (r0 + RPB <= N) {
+          dma16_so(base[t] + r0 * rs[t], off[t], lds);
+        } else {
+          const int row = min(r0 + jl, N - 1);
+          dma16(base[t] + row * rs[t] + (off[t] - jl * (int)rs[t]), lds);
+        }
+        (void)lane;
+      }
+  }
+};
+
+// Per-lane byte offsets (inside one tile) of the two operand read patterns.
+template <int D, int TS>
+struct Reader {
+  typedef SwTile<D, TS> W;
+  static constexpr int NKS = D / 16;  // k-steps of a contraction over d
+  static constexpr int NDB = D / 32;  // 32-column blocks of d
+  int row[NKS];                       // ds_read_b128 for k-step ks, sub-tile 0
+  int tr[NDB][2];                     // ds_read_b64_tr_b16 for d-block db, half koff/4
+
+  __device__ inline void init() {
+    const int l = lane_id();
+    const int m = l & 31, h = l >> 5;
+    const int j = sig(m);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) row[ks] = W::off(j, 2 * ks + h);
+    const int g = l >> 4, r = l & 15;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int jj = 8 * (g >> 1) + 4 * kh + (r >> 2);
+        const int q = 4 * db + 2 * (g & 1) + ((r & 3) >> 1);
+        tr[db][kh] = W::off(jj, q) + 8 * (r & 1);
+      }
+  }
+};
+
+// A operand of a contraction over d: streamed rows sub*32 + sig(m), k-step ks.
+template <int D, int TS>
+__device__ inline bf16x8 rd_row(const char* tile, const Reader<D, TS>& rd, int sub, int ks) {
+  return *reinterpret_cast<const bf16x8*>(tile + rd.row[ks] + sub * 32 * D * 2);
+}
+
+// A operand of a contraction over the streamed rows: d-columns db*32 + m,
+// streamed rows sub*32 + 16*s + 8*h + e, e = 0..7.
+template <int D, int TS>
+__device__ inline bf16x8 rd_tr(const char* tile, const Reader<D, TS>& rd, int sub, int db, int s) {
+  const int base = (sub * 32 + 16 * s) * D * 2;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + rd.tr[db][0] + base));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + rd.tr[db][1] + base));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+}  // namespace fa

@@ -21,7 +21,7 @@
  * dimension is contiguous (stride 1).  Element (b, h, n, c) lives at
  * ptr[b*stride_b + h*stride_h + n*stride_n + c].  Pointers must be 16-byte
  * aligned and stride_n, stride_h, stride_b must be multiples of 16 bytes
- * (8 bf16 or 4 fp32 elements); stride_n >= d.  Inputs Q, K, V, dO, U_Q,
+ * (8 bf16 or 4 fp32 elements); d <= stride_n <= 2^26.  Inputs Q, K, V, dO, U_Q,
  * U_K, U_V use the problem's input dtype (bf16 or fp32).  O and every
  * output are fp32.
  *
