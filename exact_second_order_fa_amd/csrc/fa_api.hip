@@ -152,9 +152,13 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
       hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
                          dim3(fa::kThreads), 0, st, a);
   }
-  if (phase < 0 || phase == 2)
-    hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads),
-                       0, st, a);
+  if (phase < 0 || phase == 2) {
+    if constexpr (sizeof(T) == 2 && D == 64)
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
+                         dim3(fa::kThreads), 0, st, a);
+  }
 }
 
 }  // namespace
@@ -186,7 +190,8 @@ size_t fa_bwd_workspace_bytes(const fa_problem* p) {
 size_t fa_bob_workspace_bytes(const fa_problem* p) {
   Ctx c;
   if (check_problem(p, &c) != FA_OK) return 0;
-  return 3 * (size_t)(c.B * c.H * c.N) * sizeof(float);
+  const size_t padded = (size_t)((c.N + fa::kPsRows - 1) / fa::kPsRows) * fa::kPsRows;
+  return (3 * (size_t)(c.B * c.H * c.N) + 4 * (size_t)(c.B * c.H) * padded) * sizeof(float);
 }
 
 fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
@@ -292,6 +297,7 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   a.D = reinterpret_cast<float*>(workspace);
   a.alpha = a.D + nrow;
   a.E = a.D + 2 * nrow;
+  a.ps = a.D + 3 * nrow;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const bool rho1 = c.rho == 1.0f;

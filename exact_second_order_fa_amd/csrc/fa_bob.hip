@@ -62,6 +62,12 @@ __device__ inline void acc_fence(f32x16 (&a)[NDB], f32x16 (&b)[NDB], f32x16 (&c)
     asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[db]), "+a"(b[db]), "+a"(c[db]), "+a"(d[db]));
 }
 
+template <int NDB>
+__device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[db]), "+a"(b[db]));
+}
+
 // ---------------------------------------------------------------------------
 // Pass 1 (row-major).  Resident per wave: query rows i with q_i, u_Q,i
 // (scaled by pow2), do_i, L_i, D_i.  Streamed: K, V, U_K, U_V.  Per 32 x 32
@@ -224,6 +230,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     a.alpha[rv + row] = alpha;
     a.E[rv + row] = eo - alpha * Di;
   }
+  if (hh == 0) {
+    // Chain inits of the column pass for this row (see bob_pass2_dma_kernel):
+    // -L/rho, -D, -alpha/rho, -(alpha D + E) = -E°; rows past N get
+    // (-inf, 0, 0, 0), which masks them there.
+    float* ps = a.ps + ((int64_t)wk.bh * ((N + kPsRows - 1) / kPsRows) + row / kPsRows) * 4 * kPsRows + row % kPsRows;
+    const bool ok = row < N;
+    const float irho = 1.0f / a.rho;
+    ps[0] = ok ? -Li * irho : -INFINITY;
+    ps[kPsRows] = ok ? -Di : 0.0f;
+    ps[2 * kPsRows] = ok ? -alpha * irho : 0.0f;
+    ps[3 * kPsRows] = ok ? -eo : 0.0f;
+  }
   const HeadPtr<float> o = head_of<float>(a.o, wk.b, wk.h);
   float* gq = head_out(a.r0, wk.b, wk.h);
   float* gdo = head_out(a.r3, wk.b, wk.h);
@@ -242,6 +260,149 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx] - alpha * ov[idx]; });
     store_out(gq, a.r0.sn, row, N, db,
               [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eo * abk[db][idx]); });
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Pass 2 (column-major).  Resident per wave: 32 key rows j with k_j, u_K,j
+// (scaled by pow2), v_j, u_V,j.  Streamed: Q, dO, U_Q, and per streamed row
+// the chain inits written by pass 1: -L/rho, -D, -alpha/rho, -(alpha D + E).
+// Per 32 x 32 sub-tile (streamed index i on M):
+//   s = (tau S - L)/rho,  h/rho = (F - alpha)/rho,  dPD = dP - D,
+//   C' = C - alpha D - E,
+//   P = exp(tau S - L),   d~P - E = C' + h dPD,
+//   d~S = P (d~P - E),    dS = P dPD,    W = P h,
+//   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
+// Same tile schedule as pass 1.
+template <int D, int TS, bool RHO1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_dma_kernel(Args a) {
+  typedef SwTile<D, TS> W;
+  constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
+  constexpr int NSLICE = 2 * NDB;
+  constexpr int TBYTES = 3 * W::BYTES;
+  constexpr int SBYTES = 4 * kPsRows * 4;
+  constexpr int STAGE = TBYTES + SBYTES;
+  static_assert(TS == kPsRows, "one staged scalar block per tile");
+  static_assert(SBYTES % 1024 == 0, "scalar block = whole wave copies");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<bf16> k = head_of<bf16>(a.k, wk.b, wk.h), v = head_of<bf16>(a.v, wk.b, wk.h),
+                      uk = head_of<bf16>(a.uk, wk.b, wk.h), uv = head_of<bf16>(a.uv, wk.b, wk.h);
+  HeadPtr<bf16> src[3] = {head_of<bf16>(a.q, wk.b, wk.h), head_of<bf16>(a.dout, wk.b, wk.h),
+                          head_of<bf16>(a.uq, wk.b, wk.h)};
+  const int nt = (N + TS - 1) / TS;
+  const float* psh = a.ps + (int64_t)wk.bh * nt * 4 * kPsRows;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  Dma<D, TS, 3> dma;
+  dma.init(src);
+  auto copy_tile = [&](int t, const char* dst) {
+    dma.copy(t * TS, N, dst);
+    // The 2 KB of chain inits: two wave-wide copies, by waves 0 and 1.
+    if (wave < SBYTES / 1024)
+      dma16(psh + ((int64_t)t * 4 * kPsRows + wave * 256 + l * 4), lds_addr(dst + TBYTES + wave * 1024));
+  };
+  copy_tile(0, lds);
+
+  bf16x8 kf[NKS], ukf[NKS], vf[NKS], uvf[NKS];
+  load_resident<bf16, D>(kf, k.p, k.sn, col, N, a.pow2);
+  load_resident<bf16, D>(ukf, uk.p, uk.sn, col, N, a.pow2);
+  load_resident<bf16, D>(vf, v.p, v.sn, col, N, 1.0f);
+  load_resident<bf16, D>(uvf, uv.p, uv.sn, col, N, 1.0f);
+
+  Reader<D, TS> rd;
+  rd.init();
+
+  f32x16 ak[NDB], av[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ak[db] = av[db] = zero16();
+    asm volatile("" : "+a"(ak[db]), "+a"(av[db]));
+  }
+  // No load of the compiler's own may be outstanding inside the loop.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  for (int t = 0; t < nt; ++t) {
+    const char* tq = lds + (t & 1) * STAGE;
+    const char* tdo = tq + W::BYTES;
+    const char* tuq = tq + 2 * W::BYTES;
+    const float* sc = reinterpret_cast<const float*>(tq + TBYTES);
+    dma_wait();
+    __syncthreads();
+    if (t + 1 < nt) copy_tile(t + 1, lds + ((t + 1) & 1) * STAGE);
+
+    auto scores = [&](int sub, f32x16& s, f32x16& f, f32x16& dp, f32x16& c) {
+      s = row_init<TS>(sc, sub);
+      dp = row_init<TS>(sc + TS, sub);
+      f = row_init<TS>(sc + 2 * TS, sub);
+      c = row_init<TS>(sc + 3 * TS, sub);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 xq = rd_row<D, TS>(tq, rd, sub, ks);
+        const bf16x8 xuq = rd_row<D, TS>(tuq, rd, sub, ks);
+        const bf16x8 xd = rd_row<D, TS>(tdo, rd, sub, ks);
+        mfma_v(s, xq, kf[ks]);
+        mfma_v(f, xuq, kf[ks]);
+        mfma_v(f, xq, ukf[ks]);
+        mfma_v(dp, xd, vf[ks]);
+        mfma_v(c, xd, uvf[ks]);
+      }
+    };
+    auto acc_slice = [&](int sub, int sl, const Chain<bf16>& cdt, const Chain<bf16>& cds, const Chain<bf16>& cw) {
+      const int db = sl >> 1, s2 = sl & 1;
+      const bf16x8 xq = rd_tr<D, TS>(tq, rd, sub, db, s2);
+      const bf16x8 xuq = rd_tr<D, TS>(tuq, rd, sub, db, s2);
+      const bf16x8 xd = rd_tr<D, TS>(tdo, rd, sub, db, s2);
+      mfma_acc(ak[db], xq, cdt.f[s2]);
+      mfma_acc(ak[db], xuq, cds.f[s2]);
+      mfma_acc(av[db], xd, cw.f[s2]);
+    };
+
+    f32x16 s, f, dp, c;
+    scores(0, s, f, dp, c);
+    Chain<bf16> pdt, pds, pw;  // chains of the previous sub-tile
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      mfma_fence(s, f, dp, c);
+      Chain<bf16> cdt, cds, cw;
+#pragma unroll
+      for (int part = 0; part < 4; ++part) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = 4 * part + e;
+          const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
+          const float h = RHO1 ? f[idx] : f[idx] * a.rho;
+          const float x = fmaf(h, dp[idx], c[idx]);
+          cdt.f[idx >> 3][idx & 7] = (bf16)(p * x);
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
+          cw.f[idx >> 3][idx & 7] = (bf16)(p * h);
+        }
+        if (sub > 0) {
+#pragma unroll
+          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl) acc_slice(sub - 1, sl, pdt, pds, pw);
+        }
+      }
+      pdt = cdt;
+      pds = cds;
+      pw = cw;
+      if (sub + 1 < NSUB) scores(sub + 1, s, f, dp, c);
+    }
+#pragma unroll
+    for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl, pdt, pds, pw);
+  }
+
+  acc_fence2<NDB>(ak, av);
+  float* gk = head_out(a.r1, wk.b, wk.h);
+  float* gv = head_out(a.r2, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_out(gk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
+    store_out(gv, a.r2.sn, col, N, db, [&](int idx) { return av[db][idx]; });
   }
 }
 

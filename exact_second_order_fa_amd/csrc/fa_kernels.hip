@@ -33,6 +33,7 @@ struct Args {
   float* D;                            // [B,H,N] rowsum(dO * O)
   float* alpha;                        // [B,H,N] BoB row scalar alpha
   float* E;                            // [B,H,N] BoB row scalar E
+  float* ps;                           // [B*H][ceil(N/128)][4][128] column-pass chain inits
   int B, H, N;
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
 };

@@ -36,6 +36,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kResRows = 32 * kWaves;  // resident rows per workgroup
+constexpr int kPsRows = 128;           // row granule of the staged column-pass scalars
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -112,7 +112,9 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor dq, fa_tensor dk, fa_tensor dv,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes fa_bob needs: D, alpha, E, each B*H*N fp32, in that order. */
+/* Workspace bytes fa_bob needs: D, alpha, E, each B*H*N fp32, in that order,
+ * then 16 * B*H*ceil(N/128)*128 bytes of per-row chain inits the row pass
+ * leaves for the column pass (an internal layout). */
 size_t fa_bob_workspace_bytes(const fa_problem* p);
 
 /*
@@ -133,8 +135,10 @@ size_t fa_bob_workspace_bytes(const fa_problem* p);
  * column-major pass writes gk, gv once per column block.  No N x N tensor is
  * written anywhere and no atomics are used, so results are deterministic.
  * In:  q, k, v, dout, uq, uk, uv (in_dtype); o (fp32), lse (fp32) from fa_fwd.
- * Out: gq, gk, gv, gdo (fp32).  Workspace: [D | alpha | E], each contiguous
- *      [B,H,N] fp32 (this layout is part of the ABI).
+ * Out: gq, gk, gv, gdo (fp32).  Workspace: [D | alpha | E | internal], D,
+ *      alpha, E each contiguous [B,H,N] fp32 (this part of the layout is part
+ *      of the ABI); the internal tail carries per-row values from the row pass
+ *      to the column pass.
  */
 fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor o, const float* lse, fa_tensor dout,

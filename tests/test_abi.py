@@ -53,7 +53,8 @@ def prob(B=1, H=2, N=100, d=64, scale=-1.0, causal=0, dt=fa.FA_BF16):
 
 def test_workspace_sizes(lib):
     p = prob(2, 3, 130, 64)
-    assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == 3 * 2 * 3 * 130 * 4
+    # D, alpha, E ([B,H,N] fp32 each), then four chain inits per row padded to 128 rows
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == (3 * 2 * 3 * 130 + 4 * 2 * 3 * 256) * 4
     assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 2 * 3 * 130 * 4
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(d=96))) == 0
     assert lib.fa_bob_workspace_bytes(None) == 0

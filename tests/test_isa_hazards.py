@@ -1,0 +1,40 @@
+"""The gfx950 assembly of the library has no unresolved matrix-core data
+hazards (see tests/isa_hazards.py for the rules).  Host-only: hipcc
+cross-compiles the device code to assembly; no GPU is used."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from exact_second_order_fa_amd import build
+from tests.isa_hazards import check_asm, check_kernel
+
+
+def test_checker_flags_planted_hazards():
+    """The checker itself: a VALU read 3 instructions after an MFMA write, a
+    VALU-written operand read by the next MFMA, and a clean sequence."""
+    bad = ["v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0",
+           "s_nop 1",
+           "v_add_f32_e32 v24, v0, v1"]
+    assert any(e.startswith("R2") for e in check_kernel(bad))
+    bad2 = ["v_mov_b32_e32 v16, 0", "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0"]
+    assert any(e.startswith("R1") for e in check_kernel(bad2))
+    good = ["v_mov_b32_e32 v16, 0", "s_nop 1",
+            "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]",
+            "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]",
+            "s_nop 7", "s_nop 3", "v_accvgpr_read_b32 v30, a3"]
+    assert check_kernel(good) == []
+
+
+@pytest.mark.skipif(not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")), reason="hipcc missing")
+def test_library_assembly_has_no_mfma_hazards(tmp_path):
+    out = tmp_path / "fa.s"
+    cmd = [build.hipcc_path(), *[f for f in build.HIPCC_FLAGS if f not in ("-shared", "-fPIC")],
+           "--cuda-device-only", "-S", "-I", build.INCLUDE, "-I", os.path.dirname(build.SRC), "-o", str(out), build.SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    found = check_asm(out.read_text())
+    assert any("bob_pass1_dma" in k for k in found) and any("bob_pass2_dma" in k for k in found)
+    bad = {k: v for k, v in found.items() if v}
+    assert not bad, {k: v[:5] for k, v in bad.items()}
