@@ -147,14 +147,22 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
   if (phase < 0 || phase == 0) launch_rowscalar<T, D>(c, a, st);
   if (phase < 0 || phase == 1) {
     if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
+                         a);
+    else if constexpr (sizeof(T) == 2 && D == 128)
+      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
+                         a);
     else
       hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
                          dim3(fa::kThreads), 0, st, a);
   }
   if (phase < 0 || phase == 2) {
     if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false>), dim3(grid_rows(c)),
+                         dim3(fa::kThreads), 0, st, a);
+    else if constexpr (sizeof(T) == 2 && D == 128)
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true>), dim3(grid_rows(c)), dim3(fa::kThreads),
+                         0, st, a);
     else
       hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
                          dim3(fa::kThreads), 0, st, a);

@@ -44,6 +44,10 @@ __device__ inline f32x16 mfma_first(bf16x8 a, bf16x8 b) {
   return d;
 }
 // d += a * b, d in VGPRs, b resident in AGPRs.
+__device__ inline void mfma_va(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
+}
+// d += a * b, all operands in VGPRs.
 __device__ inline void mfma_v(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
@@ -86,7 +90,7 @@ __device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
 // Schedule of one tile (NSUB sub-tiles): scores(0); then for each sub-tile s
 // the elementwise work of s interleaved with the accumulations of s - 1, and
 // the scores of s + 1.
-template <int D, int TS, bool RHO1>
+template <int D, int TS, bool RHO1, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_dma_kernel(Args a) {
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
@@ -169,9 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
     // One (d-block, k-step) slice of the accumulations of sub-tile `sub`.
-    auto acc_slice = [&](int sub, int sl, const Chain<bf16>& cp, const Chain<bf16>& cpf,
+    auto acc_slice = [&](int sub, int db, int s2, const Chain<bf16>& cp, const Chain<bf16>& cpf,
                          const Chain<bf16>& cpt, const Chain<bf16>& cds) {
-      const int db = sl >> 1, s2 = sl & 1;
       const bf16x8 xuv = rd_tr<D, TS>(tuv, rd, sub, db, s2);
       const bf16x8 xv = rd_tr<D, TS>(tv, rd, sub, db, s2);
       const bf16x8 xk = rd_tr<D, TS>(tk, rd, sub, db, s2);
@@ -183,6 +186,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       mfma_acc(ar[db], xk, cds.f[s2]);
       mfma_acc(abk[db], xk, cp.f[s2]);
     };
+    // Elementwise work on elements 4*part .. 4*part+3 of the current sub-tile.
+    auto elementwise = [&](int part, const f32x16& s, const f32x16& f, const f32x16& dp, const f32x16& c,
+                           Chain<bf16>& cp, Chain<bf16>& cpf, Chain<bf16>& cpt, Chain<bf16>& cds) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * part + e;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
+        const float F = RHO1 ? f[idx] : f[idx] * a.rho;
+        const float dpd = dp[idx] - Di;
+        const float t0 = fmaf(F, dpd, c[idx]);
+        const float pf = p * F, pt = p * t0;
+        alpha_p += pf;
+        eo_p += pt;
+        cp.f[idx >> 3][idx & 7] = (bf16)p;
+        cpf.f[idx >> 3][idx & 7] = (bf16)pf;
+        cpt.f[idx >> 3][idx & 7] = (bf16)pt;
+        cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
+      }
+    };
 
     f32x16 s, f, dp, c;
     scores(0, s, f, dp, c);
@@ -193,24 +215,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       Chain<bf16> cp, cpf, cpt, cds;
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
+        elementwise(part, s, f, dp, c, cp, cpf, cpt, cds);
+        if constexpr (SPLIT) {
+          // Parts 0-1 overlap the k-step-1 half of sub - 1; parts 2-3 the
+          // k-step-0 half of this sub-tile (its chains come from parts 0-1).
+          constexpr int H = NDB / 2;
+          if (part < 2) {
+            if (sub > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = 4 * part + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
-          const float F = RHO1 ? f[idx] : f[idx] * a.rho;
-          const float dpd = dp[idx] - Di;
-          const float t0 = fmaf(F, dpd, c[idx]);
-          const float pf = p * F, pt = p * t0;
-          alpha_p += pf;
-          eo_p += pt;
-          cp.f[idx >> 3][idx & 7] = (bf16)p;
-          cpf.f[idx >> 3][idx & 7] = (bf16)pf;
-          cpt.f[idx >> 3][idx & 7] = (bf16)pt;
-          cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
-        }
-        if (sub > 0) {
+              for (int db = part * H; db < (part + 1) * H; ++db) acc_slice(sub - 1, db, 1, pp, ppf, ppt, pds);
+            }
+          } else {
 #pragma unroll
-          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl) acc_slice(sub - 1, sl, pp, ppf, ppt, pds);
+            for (int db = (part - 2) * H; db < (part - 1) * H; ++db) acc_slice(sub, db, 0, cp, cpf, cpt, cds);
+          }
+        } else if (sub > 0) {
+#pragma unroll
+          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl)
+            acc_slice(sub - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds);
         }
       }
       pp = cp;
@@ -219,8 +241,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       pds = cds;
       if (sub + 1 < NSUB) scores(sub + 1, s, f, dp, c);
     }
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl, pp, ppf, ppt, pds);
+      for (int db = 0; db < NDB; ++db) acc_slice(NSUB - 1, db, 1, pp, ppf, ppt, pds);
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds);
+    }
   }
 
   acc_fence<NDB>(ag, aom, ar, abk);
@@ -275,16 +302,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   d~S = P (d~P - E),    dS = P dPD,    W = P h,
 //   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
 // Same tile schedule as pass 1.
-template <int D, int TS, bool RHO1>
+template <int D, int TS, bool RHO1, bool SPLIT, bool RESA>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_dma_kernel(Args a) {
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int NSLICE = 2 * NDB;
   constexpr int TBYTES = 3 * W::BYTES;
-  constexpr int SBYTES = 4 * kPsRows * 4;
+  constexpr int SBYTES = 4 * TS * 4;
   constexpr int STAGE = TBYTES + SBYTES;
-  static_assert(TS == kPsRows, "one staged scalar block per tile");
-  static_assert(SBYTES % 1024 == 0, "scalar block = whole wave copies");
+  static_assert(kPsRows % TS == 0 && (TS == 64 || TS == 128), "tiles split the staged scalar blocks");
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
   const Work wk = work_item(a);
@@ -296,16 +322,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   HeadPtr<bf16> src[3] = {head_of<bf16>(a.q, wk.b, wk.h), head_of<bf16>(a.dout, wk.b, wk.h),
                           head_of<bf16>(a.uq, wk.b, wk.h)};
   const int nt = (N + TS - 1) / TS;
-  const float* psh = a.ps + (int64_t)wk.bh * nt * 4 * kPsRows;
+  const float* psh = a.ps + (int64_t)wk.bh * ((N + kPsRows - 1) / kPsRows) * 4 * kPsRows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   Dma<D, TS, 3> dma;
   dma.init(src);
   auto copy_tile = [&](int t, const char* dst) {
     dma.copy(t * TS, N, dst);
-    // The 2 KB of chain inits: two wave-wide copies, by waves 0 and 1.
-    if (wave < SBYTES / 1024)
-      dma16(psh + ((int64_t)t * 4 * kPsRows + wave * 256 + l * 4), lds_addr(dst + TBYTES + wave * 1024));
+    // The tile's chain inits, [4][TS] floats: TS / 64 wave-wide copies.  Lane l
+    // of copy w moves rows 4 (l % 16) .. +3 of init (4 w + l / 16) % 4 ...
+    if (wave < SBYTES / 1024) {
+      const int r0 = t * TS;
+      const int e = (wave * 64 + l) * 4;  // float index inside the [4][TS] block
+      const int kk = e / TS, rr = e % TS;
+      const float* g = psh + ((int64_t)(r0 / kPsRows) * 4 + kk) * kPsRows + r0 % kPsRows + rr;
+      dma16(g, lds_addr(dst + TBYTES + wave * 1024));
+    }
   };
   copy_tile(0, lds);
 
@@ -314,6 +346,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   load_resident<bf16, D>(ukf, uk.p, uk.sn, col, N, a.pow2);
   load_resident<bf16, D>(vf, v.p, v.sn, col, N, 1.0f);
   load_resident<bf16, D>(uvf, uv.p, uv.sn, col, N, 1.0f);
+  if constexpr (RESA) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(vf[ks]), "+a"(uvf[ks]));
+  }
 
   Reader<D, TS> rd;
   rd.init();
@@ -349,18 +385,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mfma_v(s, xq, kf[ks]);
         mfma_v(f, xuq, kf[ks]);
         mfma_v(f, xq, ukf[ks]);
-        mfma_v(dp, xd, vf[ks]);
-        mfma_v(c, xd, uvf[ks]);
+        if constexpr (RESA) {
+          mfma_va(dp, xd, vf[ks]);
+          mfma_va(c, xd, uvf[ks]);
+        } else {
+          mfma_v(dp, xd, vf[ks]);
+          mfma_v(c, xd, uvf[ks]);
+        }
       }
     };
-    auto acc_slice = [&](int sub, int sl, const Chain<bf16>& cdt, const Chain<bf16>& cds, const Chain<bf16>& cw) {
-      const int db = sl >> 1, s2 = sl & 1;
+    auto acc_slice = [&](int sub, int db, int s2, const Chain<bf16>& cdt, const Chain<bf16>& cds,
+                         const Chain<bf16>& cw) {
       const bf16x8 xq = rd_tr<D, TS>(tq, rd, sub, db, s2);
       const bf16x8 xuq = rd_tr<D, TS>(tuq, rd, sub, db, s2);
       const bf16x8 xd = rd_tr<D, TS>(tdo, rd, sub, db, s2);
       mfma_acc(ak[db], xq, cdt.f[s2]);
       mfma_acc(ak[db], xuq, cds.f[s2]);
       mfma_acc(av[db], xd, cw.f[s2]);
+    };
+    auto elementwise = [&](int part, const f32x16& s, const f32x16& f, const f32x16& dp, const f32x16& c,
+                           Chain<bf16>& cdt, Chain<bf16>& cds, Chain<bf16>& cw) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int idx = 4 * part + e;
+        const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
+        const float h = RHO1 ? f[idx] : f[idx] * a.rho;
+        const float x = fmaf(h, dp[idx], c[idx]);
+        cdt.f[idx >> 3][idx & 7] = (bf16)(p * x);
+        cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
+        cw.f[idx >> 3][idx & 7] = (bf16)(p * h);
+      }
     };
 
     f32x16 s, f, dp, c;
@@ -372,19 +426,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       Chain<bf16> cdt, cds, cw;
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
+        elementwise(part, s, f, dp, c, cdt, cds, cw);
+        if constexpr (SPLIT) {
+          constexpr int H = NDB / 2;
+          if (part < 2) {
+            if (sub > 0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = 4 * part + e;
-          const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
-          const float h = RHO1 ? f[idx] : f[idx] * a.rho;
-          const float x = fmaf(h, dp[idx], c[idx]);
-          cdt.f[idx >> 3][idx & 7] = (bf16)(p * x);
-          cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
-          cw.f[idx >> 3][idx & 7] = (bf16)(p * h);
-        }
-        if (sub > 0) {
+              for (int db = part * H; db < (part + 1) * H; ++db) acc_slice(sub - 1, db, 1, pdt, pds, pw);
+            }
+          } else {
 #pragma unroll
-          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl) acc_slice(sub - 1, sl, pdt, pds, pw);
+            for (int db = (part - 2) * H; db < (part - 1) * H; ++db) acc_slice(sub, db, 0, cdt, cds, cw);
+          }
+        } else if (sub > 0) {
+#pragma unroll
+          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl)
+            acc_slice(sub - 1, sl >> 1, sl & 1, pdt, pds, pw);
         }
       }
       pdt = cdt;
@@ -392,8 +449,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       pw = cw;
       if (sub + 1 < NSUB) scores(sub + 1, s, f, dp, c);
     }
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl, pdt, pds, pw);
+      for (int db = 0; db < NDB; ++db) acc_slice(NSUB - 1, db, 1, pdt, pds, pw);
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pdt, pds, pw);
+    }
   }
 
   acc_fence2<NDB>(ak, av);
