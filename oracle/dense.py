@@ -1,15 +1,27 @@
 """Dense float64 oracle: every N x N matrix is materialised (use for N <= ~1024).
 
 All functions take one attention head: 2-D arrays of shape (N, d) (``q``,
-``k``, ``v``, ``do`` and the cotangents ``uq``, ``uk``, ``uv``), and the
-softmax scale ``tau``.  Non-causal attention (no mask term).
+``k``, ``v``, ``do`` and the cotangents ``uq``, ``uk``, ``uv``), the softmax
+scale ``tau`` and ``causal``.  With ``causal`` the additive mask term B_mask of
+[FlashBoB] section 3 is -inf where key j > query i and 0 elsewhere, so the
+softmax runs over the valid columns j <= i only; P is exactly 0 on the
+masked entries, which is all the later formulas need (every N x N quantity
+enters the outputs multiplied by P).
 """
 from __future__ import annotations
 
 import numpy as np
 
 
-def forward_dense(q, k, v, tau):
+def causal_mask(N):
+    """B_mask of [FlashBoB] section 3 for causal attention: -inf above the
+    diagonal (key j > query i), 0 elsewhere."""
+    m = np.zeros((N, N))
+    m[np.triu_indices(N, 1)] = -np.inf
+    return m
+
+
+def forward_dense(q, k, v, tau, causal=False):
     """Forward pass and saved log-normaliser.
 
     [FlashBoB] section 3: S = tau Q K^T, P = softmax(S) row-wise, O = P V, and
@@ -18,6 +30,8 @@ def forward_dense(q, k, v, tau):
     only to avoid overflow; it cancels exactly in L.
     """
     S = tau * (q @ k.T)
+    if causal:
+        S = S + causal_mask(S.shape[0])
     m = S.max(axis=1, keepdims=True)
     L = (m + np.log(np.exp(S - m).sum(axis=1, keepdims=True)))[:, 0]
     P = np.exp(S - L[:, None])
@@ -25,7 +39,7 @@ def forward_dense(q, k, v, tau):
     return {"S": S, "P": P, "O": O, "L": L}
 
 
-def backward_dense(q, k, v, do, tau):
+def backward_dense(q, k, v, do, tau, causal=False):
     """First backward of attention at output cotangent dO.
 
     [FlashBoB] section 3: dP = dO V^T, dV = P^T dO, dS_ij = P_ij (dP_ij - D_i),
@@ -33,7 +47,7 @@ def backward_dense(q, k, v, do, tau):
     [FA2-recompute] shows equals rowsum(dO * O).  Both forms of D are
     returned so the identity can be checked.
     """
-    f = forward_dense(q, k, v, tau)
+    f = forward_dense(q, k, v, tau, causal)
     P, O = f["P"], f["O"]
     dP = do @ v.T
     dV = P.T @ do
@@ -46,14 +60,14 @@ def backward_dense(q, k, v, do, tau):
             "dQ": dQ, "dK": dK, "dV": dV}
 
 
-def phi_dense(q, k, v, do, uq, uk, uv, tau):
+def phi_dense(q, k, v, do, uq, uk, uv, tau, causal=False):
     """The BoB functional of [FlashBoB] section 4.1:
     Phi = <dQ, U_Q> + <dK, U_K> + <dV, U_V> (Frobenius inner products)."""
-    b = backward_dense(q, k, v, do, tau)
+    b = backward_dense(q, k, v, do, tau, causal)
     return float((b["dQ"] * uq).sum() + (b["dK"] * uk).sum() + (b["dV"] * uv).sum())
 
 
-def bob_dense(q, k, v, do, uq, uk, uv, tau):
+def bob_dense(q, k, v, do, uq, uk, uv, tau, causal=False):
     """Backward-over-backward by the reverse-mode steps of [FlashBoB] appendix D.
 
     The cotangents on the first-backward outputs are U_Q, U_K, U_V (appendix D,
@@ -75,7 +89,7 @@ def bob_dense(q, k, v, do, uq, uk, uv, tau):
     outputs gQ = d~(Q), gK = d~(K), gV = d~(V), gdO = d~(dO), the row scalars
     alpha and E, and the forward/backward state.
     """
-    b = backward_dense(q, k, v, do, tau)
+    b = backward_dense(q, k, v, do, tau, causal)
     P, dP, dS, D = b["P"], b["dP"], b["dS"], b["D"]
     # Step 1
     F = tau * (uq @ k.T + q @ uk.T)

@@ -62,7 +62,15 @@ def _chunks(n, size):
     return [(s, min(n, s + size)) for s in range(0, n, size)]
 
 
-def _row_strip(q, k, v, do, uq, uk, uv, tau, rows, col_chunk, outputs):
+def _mask(rows, a, b, causal):
+    """The causal part of B_mask ([FlashBoB] section 3) for query rows ``rows``
+    and key columns a..b-1: -inf where key > query, else 0 (None if not causal)."""
+    if not causal:
+        return None
+    return np.where(np.arange(a, b)[None, :] > np.asarray(rows)[:, None], -np.inf, 0.0)
+
+
+def _row_strip(q, k, v, do, uq, uk, uv, tau, rows, col_chunk, outputs, causal=False):
     """All row quantities for the rows ``rows`` (an index array) of one head."""
     N = k.shape[0]
     Q, dO, UQ = q[rows], do[rows], uq[rows]
@@ -70,7 +78,9 @@ def _row_strip(q, k, v, do, uq, uk, uv, tau, rows, col_chunk, outputs):
     chunks = _chunks(N, col_chunk)
 
     def scores(a, b):
-        return tau * (Q @ k[a:b].T)
+        S = tau * (Q @ k[a:b].T)
+        m = _mask(rows, a, b, causal)
+        return S if m is None else S + m
 
     # sweep 1: row max
     m = np.full(R, -np.inf)
@@ -135,7 +145,7 @@ def _default_strip(N, d):
 
 
 def row_pass(q, k, v, do, uq, uk, uv, tau, rows=None, outputs="all",
-             strip=None, col_chunk=2048, threads=None):
+             strip=None, col_chunk=2048, threads=None, causal=False):
     """Row quantities of one head for the rows ``rows`` (default: all).
 
     ``outputs``: "fwd" -> L, O, D; "state" -> also alpha, E;
@@ -146,7 +156,7 @@ def row_pass(q, k, v, do, uq, uk, uv, tau, rows=None, outputs="all",
     strip = strip or _default_strip(N, q.shape[1])
     tasks = [rows[s:s + strip] for s in range(0, len(rows), strip)]
     parts = _run_pool(
-        lambda r: _row_strip(q, k, v, do, uq, uk, uv, tau, r, col_chunk, outputs),
+        lambda r: _row_strip(q, k, v, do, uq, uk, uv, tau, r, col_chunk, outputs, causal),
         tasks, threads)
     return {key: np.concatenate([p[key] for p in parts], axis=0) for key in parts[0]}
 
@@ -156,7 +166,7 @@ def row_state(q, k, v, do, uq, uk, uv, tau, **kw):
     return row_pass(q, k, v, do, uq, uk, uv, tau, outputs="state", **kw)
 
 
-def _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, cols, row_chunk):
+def _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, cols, row_chunk, causal=False):
     N, d = q.shape
     Kc, Vc, UKc, UVc = k[cols], v[cols], uk[cols], uv[cols]
     Cn = Kc.shape[0]
@@ -167,7 +177,10 @@ def _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, cols, row_chunk):
     for a, b in _chunks(N, row_chunk):
         Qi, dOi, UQi = q[a:b], do[a:b], uq[a:b]
         La, Da, Aa, Ea = L[a:b, None], D[a:b, None], alpha[a:b, None], E[a:b, None]
-        P = np.exp(tau * (Qi @ Kc.T) - La)
+        S = tau * (Qi @ Kc.T)
+        if causal:
+            S = S + np.where(np.asarray(cols)[None, :] > np.arange(a, b)[:, None], -np.inf, 0.0)
+        P = np.exp(S - La)
         F = tau * (UQi @ Kc.T + Qi @ UKc.T)
         dP = dOi @ Vc.T
         C = dOi @ UVc.T
@@ -183,7 +196,7 @@ def _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, cols, row_chunk):
 
 
 def col_pass(q, k, v, do, uq, uk, uv, tau, state, cols=None, strip=64,
-             row_chunk=2048, threads=None):
+             row_chunk=2048, threads=None, causal=False):
     """Column-owned outputs gK, gV (and dK, dV) of one head for the key
     columns ``cols`` (default: all), given the row state of every row."""
     N = k.shape[0]
@@ -191,13 +204,13 @@ def col_pass(q, k, v, do, uq, uk, uv, tau, state, cols=None, strip=64,
     tasks = [cols[s:s + strip] for s in range(0, len(cols), strip)]
     L, D, alpha, E = state["L"], state["D"], state["alpha"], state["E"]
     parts = _run_pool(
-        lambda c: _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, c, row_chunk),
+        lambda c: _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, c, row_chunk, causal),
         tasks, threads)
     return {key: np.concatenate([p[key] for p in parts], axis=0) for key in parts[0]}
 
 
 def bob_streaming(q, k, v, do, uq, uk, uv, tau, threads=None, strip=None,
-                  col_chunk=2048):
+                  col_chunk=2048, causal=False):
     """Full BoB over tensors of shape (B, H, N, d), float64.
 
     Returns a dict of (B, H, N, d) arrays gQ, gK, gV, gdO, dQ, dK, dV, O and
@@ -209,8 +222,9 @@ def bob_streaming(q, k, v, do, uq, uk, uv, tau, threads=None, strip=None,
         for hh in range(H):
             args = [t[b, hh] for t in (q, k, v, do, uq, uk, uv)]
             r = row_pass(*args, tau, outputs="all", strip=strip,
-                         col_chunk=col_chunk, threads=threads)
-            c = col_pass(*args, tau, r, threads=threads, row_chunk=col_chunk)
+                         col_chunk=col_chunk, threads=threads, causal=causal)
+            c = col_pass(*args, tau, r, threads=threads, row_chunk=col_chunk,
+                         causal=causal)
             r.update(c)
             for key, val in r.items():
                 if key not in res:

@@ -308,3 +308,108 @@ def test_bob_streaming_multihead_vs_torch():
             ref = torch_bob(*[x[b, h] for x in t], tau)
             for key in OUT_KEYS + ("dQ", "dK", "dV", "O"):
                 assert relerr(out[key][b, h], ref[key]) < 1e-12, (b, h, key)
+
+
+# ---------------------------------------------------------------- causal mask
+
+
+def torch_bob_causal(q, k, v, do, uq, uk, uv, tau):
+    """Independent reference for causal attention: float64 autograd double
+    backward with the mask applied by masked_fill before the softmax."""
+    Q, K, V, dO = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, do))
+    UQ, UK, UV = (torch.tensor(x, dtype=torch.float64) for x in (uq, uk, uv))
+    N = Q.shape[0]
+    keep = torch.ones(N, N, dtype=torch.bool).tril()
+    S = (tau * Q @ K.T).masked_fill(~keep, float("-inf"))
+    P = torch.softmax(S, dim=-1)
+    O = P @ V
+    dQ, dK, dV = torch.autograd.grad(O, (Q, K, V), dO, create_graph=True)
+    phi = (dQ * UQ).sum() + (dK * UK).sum() + (dV * UV).sum()
+    g = torch.autograd.grad(phi, (Q, K, V, dO))
+    return {"gQ": g[0].numpy(), "gK": g[1].numpy(), "gV": g[2].numpy(), "gdO": g[3].numpy(),
+            "dQ": dQ.detach().numpy(), "dK": dK.detach().numpy(), "dV": dV.detach().numpy(),
+            "O": O.detach().numpy(), "L": torch.logsumexp(S, dim=-1).detach().numpy(),
+            "phi": float(phi.detach())}
+
+
+@pytest.mark.parametrize("N,d,qk", [(1, 8, 1.0), (13, 8, 1.0), (37, 16, 1.0), (130, 64, 2.0), (64, 128, 1.0)])
+def test_causal_bob_dense_matches_torch_double_backward(N, d, qk):
+    t = head(N, d, 501 + N, qk=qk)
+    tau = 1 / np.sqrt(d)
+    ref = torch_bob_causal(*t, tau)
+    out = bob_dense(*t, tau, causal=True)
+    for key in ("O", "L", "dQ", "dK", "dV", *OUT_KEYS):
+        assert relerr(out[key], ref[key]) < 1e-11, key
+    assert abs(phi_dense(*t, tau, causal=True) - ref["phi"]) < 1e-10 * max(1, abs(ref["phi"]))
+
+
+def test_causal_bob_central_fd_of_phi_13x8():
+    """Elementwise central differences of the causal Phi."""
+    N, d = 13, 8
+    t = head(N, d, 521)
+    tau = 1 / np.sqrt(d)
+    out = bob_dense(*t, tau, causal=True)
+    eps = 1e-6
+    for idx, key in enumerate(("gQ", "gK", "gV", "gdO")):
+        fd = np.zeros((N, d))
+        for i in range(N):
+            for a in range(d):
+                p = [x.copy() for x in t]
+                m = [x.copy() for x in t]
+                p[idx][i, a] += eps
+                m[idx][i, a] -= eps
+                fd[i, a] = (phi_dense(*p, tau, causal=True) - phi_dense(*m, tau, causal=True)) / (2 * eps)
+        assert np.max(np.abs(fd - out[key])) < 2e-8 * max(1.0, np.max(np.abs(fd))), key
+
+
+def test_causal_first_row_and_last_row_closed_forms():
+    """Row 0 attends only to key 0 (P = 1, dS = 0), so gQ_0 = 0 and
+    gdO_0 = u_V,0 + (F_00 - alpha_0) v_0 = u_V,0; the last row sees every key,
+    so its forward output equals the non-causal one."""
+    N, d = 40, 16
+    t = head(N, d, 531)
+    tau = 1 / np.sqrt(d)
+    c = bob_dense(*t, tau, causal=True)
+    n = bob_dense(*t, tau)
+    assert np.max(np.abs(c["gQ"][0])) < 1e-13
+    assert np.max(np.abs(c["gdO"][0] - t[6][0])) < 1e-13
+    assert np.max(np.abs(c["O"][-1] - n["O"][-1])) < 1e-13
+    assert abs(c["L"][-1] - n["L"][-1]) < 1e-13
+
+
+def test_causal_lower_bound_instance():
+    """V = dO = U_Q = U_K = 0, U_V = W gives gdO = softmax(tau Q K^T + B_mask) W."""
+    N, d = 33, 8
+    q, k, _, _, _, _, w = head(N, d, 541)
+    z = np.zeros((N, d))
+    tau = 1 / np.sqrt(d)
+    out = bob_dense(q, k, z, z, z, z, w, tau, causal=True)
+    S = torch.tensor(q) @ torch.tensor(k).T * tau
+    S = S.masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), float("-inf"))
+    ref = torch.softmax(S, dim=-1).numpy() @ w
+    assert relerr(out["gdO"], ref) < 1e-13
+    for key in ("gQ", "gK", "gV"):
+        assert np.max(np.abs(out[key])) == 0.0, key
+
+
+@pytest.mark.parametrize("strip,chunk", [(1, 5), (7, 64), (64, 33), (None, 4096)])
+def test_causal_streaming_matches_dense(strip, chunk):
+    N, d = 150, 16
+    t = head(N, d, 551)
+    tau = 1 / np.sqrt(d)
+    ref = bob_dense(*t, tau, causal=True)
+    r = row_pass(*t, tau, outputs="all", strip=strip, col_chunk=chunk, causal=True)
+    c = col_pass(*t, tau, r, strip=strip or 64, row_chunk=chunk, causal=True)
+    for key in ("L", "O", "D", "alpha", "E", "gQ", "gdO", "dQ"):
+        assert relerr(r[key], ref[key]) < 1e-12, key
+    for key in ("gK", "gV", "dK", "dV"):
+        assert relerr(c[key], ref[key]) < 1e-12, key
+
+
+def test_causal_shift_invariance_column_sums():
+    """Adding one vector to every key shifts each valid row of scores by a
+    constant, so Phi is unchanged and sum_j gK_j = 0 under the mask too."""
+    N, d = 90, 16
+    t = head(N, d, 561)
+    out = bob_dense(*t, 1 / np.sqrt(d), causal=True)
+    assert np.max(np.abs(out["gK"].sum(axis=0))) < 1e-11 * max(1.0, np.max(np.abs(out["gK"])))
