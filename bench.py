@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_FP32_MFMA_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bob_pass1_traffic.json")
-KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_kernels.hip", "exact_second_order_fa_amd/csrc/fa_tile.h")
+KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_bob.hip", "exact_second_order_fa_amd/csrc/fa_lds.h",
+                  "exact_second_order_fa_amd/csrc/fa_kernels.hip", "exact_second_order_fa_amd/csrc/fa_tile.h")
 
 
 def kernel_source_sha() -> str:

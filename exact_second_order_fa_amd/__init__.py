@@ -156,12 +156,12 @@ def _call(name, status):
         raise FaError(status, name)
 
 
-def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
+def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, causal=False):
     """Forward: returns (O fp32 [B,H,N,d], L fp32 [B,H,N], natural-log
-    log-sum-exp of tau q.k over keys)."""
+    log-sum-exp of tau q.k over the (causally) valid keys)."""
     torch = _torch()
     B, H, N, d = _check_inputs(q, k, v)
-    p = problem(B, H, N, d, _dtype_code(q), scale)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)))
     o = _f32_like(q, o)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -170,13 +170,13 @@ def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
     return o, lse
 
 
-def bwd_workspace_bytes(B, H, N, d, in_dtype=FA_BF16) -> int:
-    p = problem(B, H, N, d, in_dtype)
+def bwd_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False) -> int:
+    p = problem(B, H, N, d, in_dtype, None, int(bool(causal)))
     return int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
 
 
-def bob_workspace_bytes(B, H, N, d, in_dtype=FA_BF16) -> int:
-    p = problem(B, H, N, d, in_dtype)
+def bob_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False) -> int:
+    p = problem(B, H, N, d, in_dtype, None, int(bool(causal)))
     return int(load_library().fa_bob_workspace_bytes(ctypes.byref(p)))
 
 
@@ -189,10 +189,11 @@ def _workspace(nbytes, device, ws):
     return ws
 
 
-def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None, stream=None):
+def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None, stream=None,
+           causal=False):
     """First backward: returns (dQ, dK, dV) fp32 and the workspace holding D."""
     B, H, N, d = _check_inputs(q, k, v, dout)
-    p = problem(B, H, N, d, _dtype_code(q), scale)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)))
     dq, dk, dv = _f32_like(q, dq), _f32_like(q, dk), _f32_like(q, dv)
     nbytes = int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
     ws = _workspace(nbytes, q.device, ws)
@@ -205,13 +206,13 @@ def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None
 
 
 def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=None, gdo=None,
-           ws=None, stream=None, phase=None):
+           ws=None, stream=None, phase=None, causal=False):
     """Backward-over-backward: gradients of <dQ,U_Q> + <dK,U_K> + <dV,U_V> with
     respect to Q, K, V and dO.  Returns (gQ, gK, gV, gdO, ws) with
     ws = [D | alpha | E], each [B, H, N] fp32.  ``phase`` (0, 1 or 2) calls
     fa_bob_phase instead, launching only that kernel."""
     B, H, N, d = _check_inputs(q, k, v, dout, uq, uk, uv)
-    p = problem(B, H, N, d, _dtype_code(q), scale)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)))
     gq, gk, gv, gdo = (_f32_like(q, x) for x in (gq, gk, gv, gdo))
     lib = load_library()
     nbytes = int(lib.fa_bob_workspace_bytes(ctypes.byref(p)))

@@ -19,6 +19,7 @@ struct Ctx {
   int64_t B, H, N, d;
   size_t esize;  // input element size
   bool bf;
+  bool causal;
   float tau, pow2, rho;
 };
 
@@ -27,7 +28,7 @@ fa_status check_problem(const fa_problem* p, Ctx* c) {
   if (p->B < 1 || p->H < 1 || p->N < 1) return FA_ERR_SHAPE;
   if (p->in_dtype != FA_BF16 && p->in_dtype != FA_FP32) return FA_ERR_DTYPE;
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
-  if (p->causal != 0) return FA_ERR_UNSUPPORTED;
+  if (p->causal != 0 && p->causal != 1) return FA_ERR_UNSUPPORTED;
   // fp32 inputs are built for d = 64 only (register budget of the fp32 MFMA path).
   if (p->in_dtype == FA_FP32 && p->d != 64) return FA_ERR_UNSUPPORTED;
   // Row vectors are indexed with 64-bit offsets, sequence positions and grid
@@ -51,6 +52,7 @@ fa_status check_problem(const fa_problem* p, Ctx* c) {
   c->N = p->N;
   c->d = p->d;
   c->bf = p->in_dtype == FA_BF16;
+  c->causal = p->causal != 0;
   c->esize = c->bf ? 2 : 4;
   c->tau = tau;
   c->pow2 = ldexpf(1.0f, ex - 1);
@@ -127,47 +129,76 @@ struct Tiles {
   static constexpr int TS = (sizeof(T) == 2 && D == 64) ? 64 : 32;
 };
 
-template <typename T, int D>
+template <typename T, int D, bool C>
 void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
-  hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+  hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool C>
 void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
   launch_rowscalar<T, D>(c, a, st);
-  hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
-  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
+  hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
                      a);
+  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
+                     st, a);
 }
 
 // phase < 0: the whole BoB (row scalars, row pass, column pass); 0, 1, 2:
 // only that kernel.
-template <typename T, int D, bool RHO1>
+template <typename T, int D, bool RHO1, bool C>
 void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
+  const dim3 g(grid_rows(c)), b(fa::kThreads);
   if (phase < 0 || phase == 0) launch_rowscalar<T, D>(c, a, st);
   if (phase < 0 || phase == 1) {
     if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
-                         a);
+      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C>), g, b, 0, st, a);
     else if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
-                         a);
+      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C>), g, b, 0, st, a);
     else
-      hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
-                         dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
   }
   if (phase < 0 || phase == 2) {
     if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false>), dim3(grid_rows(c)),
-                         dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), g, b, 0, st, a);
     else if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true>), dim3(grid_rows(c)), dim3(fa::kThreads),
-                         0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), g, b, 0, st, a);
     else
-      hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1>), dim3(grid_rows(c)),
-                         dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
   }
 }
+
+// Dispatch on (input type, d, causal).
+template <template <typename, int, bool> class L, typename... X>
+void dispatch3(const Ctx& c, X&&... x) {
+  if (c.bf) {
+    if (c.d == 64) {
+      if (c.causal) L<bf16, 64, true>::run(c, x...);
+      else L<bf16, 64, false>::run(c, x...);
+    } else {
+      if (c.causal) L<bf16, 128, true>::run(c, x...);
+      else L<bf16, 128, false>::run(c, x...);
+    }
+  } else {
+    if (c.causal) L<float, 64, true>::run(c, x...);
+    else L<float, 64, false>::run(c, x...);
+  }
+}
+
+template <typename T, int D, bool C>
+struct FwdL {
+  static void run(const Ctx& c, const Args& a, hipStream_t st) { launch_fwd<T, D, C>(c, a, st); }
+};
+template <typename T, int D, bool C>
+struct BwdL {
+  static void run(const Ctx& c, const Args& a, hipStream_t st) { launch_bwd<T, D, C>(c, a, st); }
+};
+template <typename T, int D, bool C>
+struct BobL {
+  static void run(const Ctx& c, const Args& a, hipStream_t st, int phase) {
+    if (c.rho == 1.0f) launch_bob<T, D, true, C>(c, a, st, phase);
+    else launch_bob<T, D, false, C>(c, a, st, phase);
+  }
+};
 
 }  // namespace
 
@@ -219,12 +250,7 @@ fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
   a.lse_out = lse;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (c.bf) {
-    if (c.d == 64) launch_fwd<bf16, 64>(c, a, st);
-    else launch_fwd<bf16, 128>(c, a, st);
-  } else {
-    launch_fwd<float, 64>(c, a, st);
-  }
+  dispatch3<FwdL>(c, a, st);
   return launched();
 }
 
@@ -257,12 +283,7 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
   a.D = reinterpret_cast<float*>(workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (c.bf) {
-    if (c.d == 64) launch_bwd<bf16, 64>(c, a, st);
-    else launch_bwd<bf16, 128>(c, a, st);
-  } else {
-    launch_bwd<float, 64>(c, a, st);
-  }
+  dispatch3<BwdL>(c, a, st);
   return launched();
 }
 
@@ -308,19 +329,7 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   a.ps = a.D + 3 * nrow;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  const bool rho1 = c.rho == 1.0f;
-  if (c.bf) {
-    if (c.d == 64) {
-      if (rho1) launch_bob<bf16, 64, true>(c, a, st, phase);
-      else launch_bob<bf16, 64, false>(c, a, st, phase);
-    } else {
-      if (rho1) launch_bob<bf16, 128, true>(c, a, st, phase);
-      else launch_bob<bf16, 128, false>(c, a, st, phase);
-    }
-  } else {
-    if (rho1) launch_bob<float, 64, true>(c, a, st, phase);
-    else launch_bob<float, 64, false>(c, a, st, phase);
-  }
+  dispatch3<BobL>(c, a, st, phase);
   return launched();
 }
 

@@ -12,6 +12,8 @@
 // 32-row sub-tiles are software pipelined: while the elementwise work of
 // sub-tile s runs on the VALU, the MFMA pipe computes the scores of s + 1 and
 // the accumulations of s - 1.
+#include <type_traits>
+
 #include "fa_lds.h"
 
 namespace fa {
@@ -90,7 +92,7 @@ __device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
 // Schedule of one tile (NSUB sub-tiles): scores(0); then for each sub-tile s
 // the elementwise work of s interleaved with the accumulations of s - 1, and
 // the scores of s + 1.
-template <int D, int TS, bool RHO1, bool SPLIT>
+template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_dma_kernel(Args a) {
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int STAGE = 4 * W::BYTES;
   static_assert(NSLICE == 4 || NSLICE == 8, "slices");
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
-  __shared__ __attribute__((aligned(16))) float kbias[2][TS];  // [0]: all valid, [1]: last tile
+  __shared__ __attribute__((aligned(16))) float kbias[TS];  // chain init of a ragged last tile
 
   const Work wk = work_item(a);
   const int N = a.N;
@@ -109,13 +111,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, wk.b, wk.h), head_of<bf16>(a.v, wk.b, wk.h),
                           head_of<bf16>(a.uk, wk.b, wk.h), head_of<bf16>(a.uv, wk.b, wk.h)};
   const int nt = (N + TS - 1) / TS;
+  // Causal: key tiles past this row block's last row are skipped, and the
+  // tiles from t_diag on cross the diagonal and are masked element by element.
+  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
+  const int t_diag = CAUSAL ? wk.rb * kResRows / TS : nt;
+  const bool ragged = !CAUSAL && (N % TS) != 0;
 
   // Start the first tile's copy before anything else.
   Dma<D, TS, 4> dma;
   dma.init(src);
   dma.copy(0, N, lds);
-  fill_bias<TS>(kbias[0], 0, 1 << 30);
-  fill_bias<TS>(kbias[1], (nt - 1) * TS, N);
+  fill_bias<TS>(kbias, (nt - 1) * TS, N);
 
   bf16x8 qf[NKS], uqf[NKS], df[NKS];
   load_resident<bf16, D>(qf, q.p, q.sn, row, N, a.pow2);
@@ -139,27 +145,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // No load of the compiler's own may be outstanding inside the loop.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  for (int t = 0; t < nt; ++t) {
+  // Tile modes: 0 = every key valid, 1 = ragged last tile (chain init from
+  // kbias), 2 = causal diagonal tile (chain init -inf where key > query).
+  auto tile_body = [&](int t, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     const char* tk = lds + (t & 1) * STAGE;
     const char* tv = tk + W::BYTES;
     const char* tuk = tk + 2 * W::BYTES;
     const char* tuv = tk + 3 * W::BYTES;
-    const float* kb = kbias[t == nt - 1 ? 1 : 0];
-    // This wave's copies of tile t are done; the barrier makes every wave's
-    // copies visible and guarantees that no wave still reads `next`.
-    dma_wait();
-    __syncthreads();
-    if (t + 1 < nt) dma.copy((t + 1) * TS, N, lds + ((t + 1) & 1) * STAGE);
 
     auto scores = [&](int sub, f32x16& s, f32x16& f, f32x16& dp, f32x16& c) {
-      s = row_init<TS>(kb, sub);
+      if constexpr (MODE == 1) {
+        s = row_init<TS>(kbias, sub);
+      } else if constexpr (MODE == 2) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx)
+          s[idx] = (t * TS + sub * 32 + acc_pos(idx, hh) <= row) ? 0.0f : -INFINITY;
+        asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
+      }
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 xk = rd_row<D, TS>(tk, rd, sub, ks);
         const bf16x8 xuk = rd_row<D, TS>(tuk, rd, sub, ks);
         const bf16x8 xv = rd_row<D, TS>(tv, rd, sub, ks);
         const bf16x8 xuv = rd_row<D, TS>(tuv, rd, sub, ks);
-        mfma_v(s, xk, qf[ks]);
+        if (MODE == 0 && ks == 0) {
+          s = mfma_first(xk, qf[0]);
+        } else {
+          mfma_v(s, xk, qf[ks]);
+        }
         if (ks == 0) {
           f = mfma_first(xk, uqf[0]);
           dp = mfma_first(xv, df[0]);
@@ -248,6 +262,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds);
     }
+  };
+
+  // Tiles [t0, t1) in one mode.  Each mode is its own loop, so the
+  // accumulators keep one register assignment per loop; the fence at the end
+  // covers any copy the compiler places between loops.
+  auto run = [&](int t0, int t1, auto mode_c) {
+    for (int t = t0; t < t1; ++t) {
+      // This wave's copies of tile t are done; the barrier makes every
+      // wave's copies visible and guarantees that no wave still reads the
+      // other stage.
+      dma_wait();
+      __syncthreads();
+      if (t + 1 < t_end) dma.copy((t + 1) * TS, N, lds + ((t + 1) & 1) * STAGE);
+      tile_body(t, mode_c);
+    }
+    acc_fence<NDB>(ag, aom, ar, abk);
+  };
+  if constexpr (CAUSAL) {
+    run(0, t_diag, std::integral_constant<int, 0>{});
+    run(t_diag, t_end, std::integral_constant<int, 2>{});
+  } else {
+    run(0, ragged ? nt - 1 : nt, std::integral_constant<int, 0>{});
+    if (ragged) run(nt - 1, nt, std::integral_constant<int, 1>{});
   }
 
   acc_fence<NDB>(ag, aom, ar, abk);
@@ -302,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   d~S = P (d~P - E),    dS = P dPD,    W = P h,
 //   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
 // Same tile schedule as pass 1.
-template <int D, int TS, bool RHO1, bool SPLIT, bool RESA>
+template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_dma_kernel(Args a) {
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
@@ -339,7 +376,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       dma16(g, lds_addr(dst + TBYTES + wave * 1024));
     }
   };
-  copy_tile(0, lds);
+  // Causal: query tiles before this key block's first key are skipped; tiles
+  // below t_diag cross the diagonal and are masked element by element.
+  const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
+  const int t_diag = CAUSAL ? (wk.rb * kResRows + kResRows + TS - 1) / TS : 0;
+  copy_tile(t_begin, lds + (t_begin & 1) * STAGE);
 
   bf16x8 kf[NKS], ukf[NKS], vf[NKS], uvf[NKS];
   load_resident<bf16, D>(kf, k.p, k.sn, col, N, a.pow2);
@@ -363,17 +404,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // No load of the compiler's own may be outstanding inside the loop.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  for (int t = 0; t < nt; ++t) {
+  // Tile modes: 0 = rows masked only through the staged inits, 2 = causal
+  // diagonal tile (also -inf where query < key).
+  auto tile_body = [&](int t, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
     const char* tq = lds + (t & 1) * STAGE;
     const char* tdo = tq + W::BYTES;
     const char* tuq = tq + 2 * W::BYTES;
     const float* sc = reinterpret_cast<const float*>(tq + TBYTES);
-    dma_wait();
-    __syncthreads();
-    if (t + 1 < nt) copy_tile(t + 1, lds + ((t + 1) & 1) * STAGE);
 
     auto scores = [&](int sub, f32x16& s, f32x16& f, f32x16& dp, f32x16& c) {
       s = row_init<TS>(sc, sub);
+      if constexpr (MODE == 2) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx)
+          if (t * TS + sub * 32 + acc_pos(idx, hh) < col) s[idx] = -INFINITY;
+        asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
+      }
       dp = row_init<TS>(sc + TS, sub);
       f = row_init<TS>(sc + 2 * TS, sub);
       c = row_init<TS>(sc + 3 * TS, sub);
@@ -456,7 +503,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pdt, pds, pw);
     }
-  }
+  };
+
+  auto run = [&](int t0, int t1, auto mode_c) {
+    for (int t = t0; t < t1; ++t) {
+      dma_wait();
+      __syncthreads();
+      if (t + 1 < nt) copy_tile(t + 1, lds + ((t + 1) & 1) * STAGE);
+      tile_body(t, mode_c);
+    }
+    acc_fence2<NDB>(ak, av);
+  };
+  if constexpr (CAUSAL) run(t_begin, min(t_diag, nt), std::integral_constant<int, 2>{});
+  run(CAUSAL ? min(t_diag, nt) : 0, nt, std::integral_constant<int, 0>{});
 
   acc_fence2<NDB>(ak, av);
   float* gk = head_out(a.r1, wk.b, wk.h);

@@ -109,6 +109,32 @@ __device__ inline f32x16 row_init(const float* sc, int sub) {
   return r;
 }
 
+// Causal attention ([FlashBoB] section 3, B_mask = -inf for key > query):
+// the S-chain init of a sub-tile with keys streamed (row-side kernels) or
+// queries streamed (column-side kernels) gets -inf on the masked entries.
+template <int TS, bool CAUSAL>
+__device__ inline f32x16 key_init(const float* kb, int sub, int key0, int row) {
+  f32x16 r = row_init<TS>(kb, sub);
+  if constexpr (CAUSAL) {
+    const int hh = lane_id() >> 5;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx)
+      if (key0 + sub * 32 + acc_pos(idx, hh) > row) r[idx] = -INFINITY;
+  }
+  return r;
+}
+template <int TS, bool CAUSAL>
+__device__ inline f32x16 query_init(const float* sc, int sub, int q0, int col) {
+  f32x16 r = row_init<TS>(sc, sub);
+  if constexpr (CAUSAL) {
+    const int hh = lane_id() >> 5;
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx)
+      if (q0 + sub * 32 + acc_pos(idx, hh) < col) r[idx] = -INFINITY;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Row-scalar preprocessing: D_i = sum_c dO_ic O_ic ([FA2-recompute]; the
 // first backward's D_i = sum_j P_ij dP_ij).  HBM-bound: D/8 lanes per row,
@@ -159,7 +185,7 @@ __global__ __launch_bounds__(256) void rowscalar_kernel(Args a) {
 // Forward ([FlashBoB] section 3; online softmax as in [FA2-triton]).
 // Resident: 32 query rows per wave.  Streamed: K (row copy, for S^T = K Q^T)
 // and V (transposed copy, for O^T += V^T P^T).  Running max in base-2 units.
-template <typename T, int D, int TS>
+template <typename T, int D, int TS, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -184,6 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 2> st;
   const int nt = (N + TS - 1) / TS;
+  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
   ScalarStager<TS, 1> ks;
   auto kvalid = [](int, float* o) { o[0] = 0.0f; };
   auto kpad = [](float* o) { o[0] = -INFINITY; };
@@ -192,8 +219,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   st.store(lds[0]);
   ks.store(kbias[0]);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) {
+  for (int t = 0; t < t_end; ++t) {
+    if (t + 1 < t_end) {
       st.load(src, (t + 1) * TS, N);
       ks.load((t + 1) * TS, N, kvalid, kpad);
     }
@@ -202,7 +229,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* vt = lds[t & 1] + S::ELEMS + S::ROW_ELEMS;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, row_init<TS>(kb, sub));
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
       float z[16];
       float mx = -INFINITY;
 #pragma unroll
@@ -233,7 +260,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int s2 = 0; s2 < KS32; ++s2) acc[db] = E::mma(tr_frag<T, D, TS>(vt, db, sub, s2), cp.f[s2], acc[db]);
       }
     }
-    if (t + 1 < nt) {
+    if (t + 1 < t_end) {
       st.store(lds[(t + 1) & 1]);
       ks.store(kbias[(t + 1) & 1]);
     }
@@ -250,7 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // First backward, row side: dQ = tau dS K with dS = P (dP - D)
 // ([FlashBoB] section 3).  Resident: query rows.  Streamed: K, V.
-template <typename T, int D, int TS>
+template <typename T, int D, int TS, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -279,6 +306,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 2> st;
   const int nt = (N + TS - 1) / TS;
+  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
   ScalarStager<TS, 1> ks;
   auto kvalid = [](int, float* o) { o[0] = 0.0f; };
   auto kpad = [](float* o) { o[0] = -INFINITY; };
@@ -287,8 +315,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   st.store(lds[0]);
   ks.store(kbias[0]);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) {
+  for (int t = 0; t < t_end; ++t) {
+    if (t + 1 < t_end) {
       st.load(src, (t + 1) * TS, N);
       ks.load((t + 1) * TS, N, kvalid, kpad);
     }
@@ -298,7 +326,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* vr = kr + S::ELEMS;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, row_init<TS>(kb, sub));
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
       float ds[16];
 #pragma unroll
@@ -313,7 +341,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int s2 = 0; s2 < KS32; ++s2) acc[db] = E::mma(tr_frag<T, D, TS>(kt, db, sub, s2), cds.f[s2], acc[db]);
     }
-    if (t + 1 < nt) {
+    if (t + 1 < t_end) {
       st.store(lds[(t + 1) & 1]);
       ks.store(kbias[(t + 1) & 1]);
     }
@@ -327,7 +355,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // First backward, column side: dV = P^T dO, dK = tau dS^T Q
 // ([FlashBoB] section 3).  Resident: key rows.  Streamed: Q, dO and the row
 // scalars (-L/rho, -D).
-template <typename T, int D, int TS>
+template <typename T, int D, int TS, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -363,12 +391,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   Stager<T, D, TS, 2> st;
   ScalarStager<TS, 2> ss;
   const int nt = (N + TS - 1) / TS;
-  st.load(src, 0, N);
-  ss.load(0, N, scal, pad);
-  st.store(lds[0]);
-  ss.store(scl[0]);
+  const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
+  st.load(src, t_begin * TS, N);
+  ss.load(t_begin * TS, N, scal, pad);
+  st.store(lds[t_begin & 1]);
+  ss.store(scl[t_begin & 1]);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
+  for (int t = t_begin; t < nt; ++t) {
     if (t + 1 < nt) {
       st.load(src, (t + 1) * TS, N);
       ss.load((t + 1) * TS, N, scal, pad);
@@ -380,7 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float* sc = scl[t & 1];
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, row_init<TS>(sc, sub));
+      const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
       const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
       float p[16], ds[16];
 #pragma unroll
@@ -431,7 +460,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Epilogue (the corrections of section 4.2, with R = R' + D Bk so that
 // alpha R + E Bk = alpha R' + E° Bk):
 //     E = E° - alpha D,  gdo = G - alpha o,  gq = tau (Om - alpha R' - E° Bk).
-template <typename T, int D, int TS, bool RHO1>
+template <typename T, int D, int TS, bool RHO1, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -464,6 +493,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 4> st;
   const int nt = (N + TS - 1) / TS;
+  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
   ScalarStager<TS, 1> ks;
   auto kvalid = [](int, float* o) { o[0] = 0.0f; };
   auto kpad = [](float* o) { o[0] = -INFINITY; };
@@ -472,8 +502,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   st.store(lds[0]);
   ks.store(kbias[0]);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    if (t + 1 < nt) {
+  for (int t = 0; t < t_end; ++t) {
+    if (t + 1 < t_end) {
       st.load(src, (t + 1) * TS, N);
       ks.load((t + 1) * TS, N, kvalid, kpad);
     }
@@ -488,7 +518,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* uvt = uvr + S::ROW_ELEMS;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, row_init<TS>(kb, sub));
+      const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
       f32x16 f = mm_row<T, D, TS>(kr, sub, uqf, zero16());
       f = mm_row<T, D, TS>(ukr, sub, qf, f);
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
@@ -528,7 +558,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           abk[db] = E::mma(xk, cp.f[s2], abk[db]);
         }
     }
-    if (t + 1 < nt) {
+    if (t + 1 < t_end) {
       st.store(lds[(t + 1) & 1]);
       ks.store(kbias[(t + 1) & 1]);
     }
@@ -573,7 +603,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   P = exp(tau S - L),   d~P - E = C' + h dPD,
 //   d~S = P (d~P - E),    dS = P dPD,    W = P h,
 //   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
-template <typename T, int D, int TS, bool RHO1>
+template <typename T, int D, int TS, bool RHO1, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -615,12 +645,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   Stager<T, D, TS, 3> st;
   ScalarStager<TS, 4> ss;
   const int nt = (N + TS - 1) / TS;
-  st.load(src, 0, N);
-  ss.load(0, N, scal, pad);
-  st.store(lds[0]);
-  ss.store(scl[0]);
+  const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
+  st.load(src, t_begin * TS, N);
+  ss.load(t_begin * TS, N, scal, pad);
+  st.store(lds[t_begin & 1]);
+  ss.store(scl[t_begin & 1]);
   __syncthreads();
-  for (int t = 0; t < nt; ++t) {
+  for (int t = t_begin; t < nt; ++t) {
     if (t + 1 < nt) {
       st.load(src, (t + 1) * TS, N);
       ss.load((t + 1) * TS, N, scal, pad);
@@ -634,7 +665,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float* sc = scl[t & 1];
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, row_init<TS>(sc, sub));
+      const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
       f32x16 f = mm_row<T, D, TS>(uqr, sub, kf, row_init<TS>(sc + 2 * TS, sub));
       f = mm_row<T, D, TS>(qr, sub, ukf, f);
       const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));

@@ -13,8 +13,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Problem: B batches x H heads, sequence length N (queries = keys), head
- * dimension d, softmax scale tau, non-causal.  One attention head is the
- * (b, h) slice.
+ * dimension d, softmax scale tau, full or causal attention.  Causal adds the
+ * mask term B_mask = -inf for key j > query i to S ([FlashBoB] section 3);
+ * key tiles entirely above the diagonal are skipped.  One attention head is
+ * the (b, h) slice.
  *
  * Tensors: every N x d operand is passed as an fa_tensor: a DEVICE pointer
  * plus element strides for the batch, head and sequence dimensions; the head
@@ -54,7 +56,7 @@ typedef enum fa_status {
   FA_ERR_SHAPE = 2,       /* B, H or N < 1, or sizes overflow */
   FA_ERR_STRIDE = 3,      /* stride or alignment rule violated */
   FA_ERR_DTYPE = 4,       /* unknown input dtype */
-  FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128}, causal != 0, or a non-finite/negative scale */
+  FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128}, causal not 0/1, or a non-finite/negative scale */
   FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   FA_ERR_HIP = 7          /* the HIP runtime reported a launch error */
 } fa_status;
@@ -67,7 +69,7 @@ typedef enum fa_dtype {
 typedef struct fa_problem {
   int64_t B, H, N, d;
   float scale;      /* tau; a value <= 0 selects 1/sqrt(d) */
-  int32_t causal;   /* must be 0 */
+  int32_t causal;   /* 0: full attention; 1: causal (key j > query i masked) */
   int32_t in_dtype; /* an fa_dtype */
 } fa_problem;
 

@@ -39,7 +39,7 @@ def to_device(raw, dtype, layout="bhnd"):
     return out
 
 
-def run_path(t, scale=None, with_bwd=True, layout="bhnd"):
+def run_path(t, scale=None, with_bwd=True, layout="bhnd", causal=False):
     """fa_fwd, fa_bwd (optional) and fa_bob on device tensors; returns torch
     tensors on the GPU."""
     import torch
@@ -52,16 +52,17 @@ def run_path(t, scale=None, with_bwd=True, layout="bhnd"):
             return torch.empty((B, N, H, d), dtype=torch.float32, device=x.device).permute(0, 2, 1, 3)
         return torch.empty(x.shape, dtype=torch.float32, device=x.device)
 
-    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], scale=scale, o=empty_like_out(t["q"]))
+    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], scale=scale, o=empty_like_out(t["q"]), causal=causal)
     res = {"O": o, "L": lse}
     if with_bwd:
         dq, dk, dv, _ = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale=scale,
                                   dq=empty_like_out(t["q"]), dk=empty_like_out(t["q"]),
-                                  dv=empty_like_out(t["q"]))
+                                  dv=empty_like_out(t["q"]), causal=causal)
         res.update(dQ=dq, dK=dk, dV=dv)
     outs = [empty_like_out(t["q"]) for _ in range(4)]
     gq, gk, gv, gdo, ws = fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"],
-                                    scale=scale, gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3])
+                                    scale=scale, gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3],
+                                    causal=causal)
     B, H, N, _ = t["q"].shape
     D, alpha, E = fa.split_workspace(ws, B, H, N)
     res.update(gQ=gq, gK=gk, gV=gv, gdO=gdo, D=D, alpha=alpha, E=E)

@@ -80,7 +80,8 @@ def bob(lib, p, tensors=None, lse=FAKE, ws=FAKE, ws_bytes=1 << 30):
     (prob(dt=7), 4),
     (prob(d=96), 5),
     (prob(d=32), 5),
-    (prob(causal=1), 5),
+    (prob(causal=2), 5),
+    (prob(causal=-1), 5),
     (prob(d=128, dt=fa.FA_FP32), 5),
     (prob(scale=float("nan")), 5),
     (prob(scale=float("inf")), 5),

@@ -22,23 +22,23 @@ TOL = {"bf16": 2e-2, "fp32": 1e-4}
 ALL = ("O", "L", "dQ", "dK", "dV", "D", "alpha", "E", "gQ", "gK", "gV", "gdO")
 
 
-def oracle_heads(f64, scale):
+def oracle_heads(f64, scale, causal=False):
     B, H = f64["q"].shape[:2]
     out = {}
     for b in range(B):
         for h in range(H):
-            r = bob_dense(*(f64[n][b, h] for n in NAMES), scale)
+            r = bob_dense(*(f64[n][b, h] for n in NAMES), scale, causal=causal)
             for key in ALL:
                 out.setdefault(key, np.zeros((B, H) + r[key].shape))[b, h] = r[key]
     return out
 
 
-def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd"):
-    say(f"case B={B} H={H} N={N} d={d} {dtype} seed={seed} scale={scale} layout={layout}")
+def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd", causal=False):
+    say(f"case B={B} H={H} N={N} d={d} {dtype} seed={seed} scale={scale} layout={layout} causal={causal}")
     raw, f64 = make_inputs(B, H, N, d, seed, dtype, cot_std=cot, qk_gain=qk)
     tau = scale if scale is not None else 1.0 / np.sqrt(d)
-    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout)
-    ref = oracle_heads(f64, tau)
+    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal)
+    ref = oracle_heads(f64, tau, causal)
     errs = {k: rel(host(got[k]), ref[k]) for k in ALL}
     say("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
@@ -116,5 +116,38 @@ def test_deterministic():
     t = to_device(raw, "bf16")
     a = run_path(t)
     b = run_path(t)
+    for key in ("O", "L", "dQ", "dK", "dV", "gQ", "gK", "gV", "gdO", "alpha", "E"):
+        assert bool((a[key] == b[key]).all()), key
+
+
+# ---------------------------------------------------------------- causal attention
+
+
+@pytest.mark.parametrize("B,H,N,d", [
+    (1, 2, 100, 64),   # ragged, one tile
+    (1, 1, 37, 64),
+    (2, 1, 300, 64),   # diagonal tiles inside several row blocks
+    (1, 1, 640, 64),   # full tiles below the diagonal
+    (1, 2, 300, 128),
+    (1, 1, 513, 128),
+])
+def test_causal_bf16_shapes(B, H, N, d):
+    check_case(B, H, N, d, "bf16", 700 + N + d, causal=True)
+
+
+def test_causal_fp32():
+    check_case(1, 1, 200, 64, "fp32", 710, causal=True)
+
+
+def test_causal_strided_and_scaled():
+    check_case(1, 2, 260, 64, "bf16", 711, layout="bnhd", causal=True)
+    check_case(1, 1, 150, 64, "bf16", 712, scale=0.1, causal=True)
+
+
+def test_causal_deterministic():
+    raw, _ = make_inputs(1, 2, 333, 64, 713, "bf16")
+    t = to_device(raw, "bf16")
+    a = run_path(t, causal=True)
+    b = run_path(t, causal=True)
     for key in ("O", "L", "dQ", "dK", "dV", "gQ", "gK", "gV", "gdO", "alpha", "E"):
         assert bool((a[key] == b[key]).all()), key
