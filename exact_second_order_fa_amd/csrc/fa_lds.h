@@ -4,10 +4,13 @@
 //     moves one 16-byte granule and the wave's 64 granules land contiguously
 //     at the LDS address the instruction names, so no VGPR holds tile data.
 //   * A tile is TS rows of D bf16 (G = D/8 granules per row) with no padding;
-//     granule q of row j sits at position q ^ swz(j) of the row, which keeps
-//     both read patterns below free of LDS bank conflicts.  The swizzle is
-//     applied on the HBM side: the lane that fills LDS position p fetches the
-//     granule that belongs there.
+//     granule q of row j sits at position q ^ swz<G>(j) of the row, which
+//     keeps both read patterns below free of LDS bank conflicts.  The swizzle
+//     is applied on the HBM side: the lane that fills LDS position p fetches
+//     the granule that belongs there.
+//   * Bank model (measured on gfx950 with SQ_LDS_BANK_CONFLICT): 64 banks of
+//     4 bytes; ds_read_b128 serves 16 lanes per cycle, ds_read_b64 32 lanes,
+//     so each group must cover 256 distinct bytes modulo 256.
 //   * Products that contract over d read their A operand (32 streamed rows x
 //     8 consecutive d per lane) with ds_read_b128.
 //   * Products that contract over the streamed index need the transposed
@@ -26,10 +29,24 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Position of granule q inside row j is q ^ swz(j).  Rows 0-3 and 8-11 (the
-// eight rows one ds_read_b128 phase touches after the sig() row permutation)
-// get eight different positions.
-__host__ __device__ constexpr int swz(int j) { return (j + 4 * (j >> 3)) & 7; }
+// Position of granule q inside row j is q ^ swz<G>(j).
+//   * Row-major reads: one 16-lane group reads the same granule of 16
+//     consecutive rows.  G = 8 (d = 64, two rows per 256 bytes): the eight
+//     even rows and the eight odd rows of a 16-row block need distinct swz;
+//     G = 16 (one row per 256 bytes): all sixteen rows do.
+//   * Transposing reads: one 32-lane group reads granules 4c .. 4c+3 of four
+//     consecutive rows 4m .. 4m+3, so those rows must map the aligned block of
+//     four granules onto disjoint blocks: for G = 8, rows 4m and 4m+2 (and
+//     4m+1, 4m+3) differ in bit 2 of swz; for G = 16 the four rows differ in
+//     bits 2-3.
+template <int G>
+__host__ __device__ constexpr int swz(int j) {
+  if constexpr (G == 8) {
+    return ((j & 2) << 1) | ((j >> 2) & 3);
+  } else {
+    return ((j & 3) << 2) | ((j >> 2) & 3);
+  }
+}
 
 template <int D, int TS>
 struct SwTile {
@@ -41,7 +58,8 @@ struct SwTile {
   static constexpr int ROWS_PER_BLOCK = 64 / G;
 
   // Byte offset of (row j, granule q).
-  __host__ __device__ static constexpr int off(int j, int q) { return (j * G + (q ^ swz(j))) * 16; }
+  static_assert(G == 8 || G == 16, "d = 64 or 128");
+  __host__ __device__ static constexpr int off(int j, int q) { return (j * G + (q ^ swz<G>(j))) * 16; }
 };
 
 // One wave-wide HBM -> LDS copy: lane i moves 16 bytes to lds_base + 16 i.
@@ -83,7 +101,8 @@ struct Dma {
   static constexpr int RPB = W::ROWS_PER_BLOCK;
   static constexpr int PER_WAVE = W::BLOCKS / NW;
   static_assert(W::BLOCKS % NW == 0, "blocks per tensor must split evenly over the waves");
-  // The swizzle of a row then depends only on the lane and the wave.
+  // Rows of one wave's blocks are 16 apart, and the swizzle depends on the
+  // row modulo 16 only, so it is fixed per lane and wave.
   static_assert((NW * RPB) % 16 == 0, "block stride must keep the row swizzle");
 
   const char* base[NT];  // head base pointers (uniform)
@@ -95,7 +114,7 @@ struct Dma {
     const int lane = lane_id();
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     jl = lane / W::G;
-    const int q = (lane % W::G) ^ swz(wave * RPB + jl);
+    const int q = (lane % W::G) ^ swz<W::G>(wave * RPB + jl);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       base[t] = reinterpret_cast<const char*>(src[t].p);

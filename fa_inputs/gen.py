@@ -36,9 +36,11 @@ class Workload:
         contract over the key index with two products each for gdO and the
         Omega term plus one each for R and B (11 in all).  Column pass: S, F
         (two), dP, C, then gK (two) and gV (one), 8 in all.  Each contraction
-        is 2 N^2 d flops, so 38 B H N^2 d for non-causal attention.
+        is 2 N^2 d flops, so 38 B H N^2 d for non-causal attention; causal
+        attention keeps half of the score entries and counts half of that.
         """
-        return 38.0 * self.B * self.H * self.N * self.N * self.d
+        f = 38.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
 
 
 WORKLOADS = {
@@ -48,6 +50,11 @@ WORKLOADS = {
     "hd128": Workload("hd128", 1, 16, 16384, 128, "bf16", 2, cot_std=0.1),
     "long": Workload("long", 1, 4, 65536, 64, "bf16", 3, qk_gain=2.0),
     "max": Workload("max", 1, 1, 262144, 64, "bf16", 4),
+    # The isolated-layer shape of the FlashBoB benchmarks (batch 4, 12 heads,
+    # causal); the pages state no input distribution, N(0,1) is used.
+    "gpt2c_4k": Workload("gpt2c_4k", 4, 12, 4096, 64, "bf16", 5, causal=True),
+    "gpt2c_16k": Workload("gpt2c_16k", 4, 12, 16384, 64, "bf16", 6, causal=True),
+    "c128_16k": Workload("c128_16k", 4, 12, 16384, 128, "bf16", 7, causal=True),
 }
 
 
@@ -71,12 +78,13 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
-                cot_std: float = 1.0, qk_gain: float = 1.0):
+                cot_std: float = 1.0, qk_gain: float = 1.0, with_f64: bool = True):
     """Draw the seven inputs.
 
     Returns ``(raw, f64)``: ``raw`` maps each name to the array the device
     receives (uint16 bf16 bits, or float32), ``f64`` maps each name to the
-    same values as float64 for the oracle.
+    same values as float64 for the oracle (``None`` values when
+    ``with_f64`` is false).
     """
     if dtype not in ("bf16", "fp32"):
         raise ValueError(f"unknown dtype {dtype!r}")
@@ -91,14 +99,14 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
         if dtype == "bf16":
             bits = f32_to_bf16_bits(x)
             raw[name] = bits
-            f64[name] = bf16_bits_to_f32(bits).astype(np.float64)
+            f64[name] = bf16_bits_to_f32(bits).astype(np.float64) if with_f64 else None
         else:
             raw[name] = x
-            f64[name] = x.astype(np.float64)
+            f64[name] = x.astype(np.float64) if with_f64 else None
     return raw, f64
 
 
-def workload_inputs(w: Workload, N: int | None = None):
+def workload_inputs(w: Workload, N: int | None = None, with_f64: bool = True):
     """Inputs of a named workload (optionally with a different length N)."""
     return make_inputs(w.B, w.H, w.N if N is None else N, w.d, w.seed, w.dtype,
-                       w.cot_std, w.qk_gain)
+                       w.cot_std, w.qk_gain, with_f64)

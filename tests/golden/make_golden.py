@@ -31,6 +31,7 @@ PLAN = {
     "hd128": ([(0, 0), (0, 15)], 24),
     "long": ([(0, 1), (0, 3)], 24),
     "max": ([(0, 0)], 32),
+    "gpt2c_16k": ([(0, 0), (3, 11)], 24),
 }
 
 
@@ -50,9 +51,9 @@ def make(name, threads):
            "L": [], "D": [], "alpha": [], "E": []}
     for (b, h) in heads:
         args = [f64[n][b, h] for n in ("q", "k", "v", "do", "uq", "uk", "uv")]
-        st = row_state(*args, w.scale, threads=threads)
+        st = row_state(*args, w.scale, threads=threads, causal=w.causal)
         cols = sample_cols(w.N, ncol, 1000 * w.seed + 17 * b + h)
-        c = col_pass(*args, w.scale, st, cols=cols, strip=8, threads=threads)
+        c = col_pass(*args, w.scale, st, cols=cols, strip=8, threads=threads, causal=w.causal)
         srows = sample_cols(w.N, ncol, 2000 * w.seed + 17 * b + h)
         for j, col in enumerate(cols):
             out["heads"].append((b, h))

@@ -62,7 +62,7 @@ def _sampled(name):
     g = np.load(path, allow_pickle=False)
     say(f"workload {name}: GPU path")
     raw, f64 = workload_inputs(w)
-    got = run_path(to_device(raw, w.dtype))
+    got = run_path(to_device(raw, w.dtype), causal=w.causal)
     del raw
     heads = sorted({tuple(x) for x in g["heads"].tolist()})
     # column-owned outputs vs stored oracle values
@@ -83,7 +83,7 @@ def _sampled(name):
         rows = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, size=22, replace=False)]))
         say(f"  oracle rows head ({b},{h})")
         r = row_pass(*(f64[n][b, h] for n in NAMES), w.scale, rows=rows, outputs="all",
-                     strip=4, threads=oracle_threads())
+                     strip=4, threads=oracle_threads(), causal=w.causal)
         for key in ("gQ", "gdO", "dQ", "O", "L", "D", "alpha", "E"):
             e = rel(host(got[key][b, h][rows]), r[key])
             say(f"  {key} head ({b},{h}) sampled rows {e:.2e}")
@@ -104,6 +104,11 @@ def test_hd128_workload_sampled():
 
 def test_long_workload_sampled():
     _sampled("long")
+
+
+def test_gpt2c_16k_causal_workload_sampled():
+    """The pages' isolated-layer shape (B=4, H=12, causal) at N=16384, d=64."""
+    _sampled("gpt2c_16k")
 
 
 def test_max_workload_sampled_and_memory():
