@@ -41,7 +41,8 @@ PAGES_MS = {
     "c128_16k": {"ms": 263.6, "gpu": "B300", "source": "FlashBoB Table 1, d=128"},
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bob_pass1_traffic.json")
-KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_bob.hip", "exact_second_order_fa_amd/csrc/fa_lds.h",
+KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_bob.hip", "exact_second_order_fa_amd/csrc/fa_bob_ws.hip",
+                  "exact_second_order_fa_amd/csrc/fa_lds.h",
                   "exact_second_order_fa_amd/csrc/fa_kernels.hip", "exact_second_order_fa_amd/csrc/fa_tile.h")
 
 

@@ -6,6 +6,7 @@
 #include "fa.h"
 #include "fa_kernels.hip"
 #include "fa_bob.hip"
+#include "fa_bob_ws.hip"
 
 namespace {
 
@@ -151,7 +152,7 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
   if (phase < 0 || phase == 0) launch_rowscalar<T, D>(c, a, st);
   if (phase < 0 || phase == 1) {
     if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C>), g, b, 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass1_ws_kernel<RHO1, C>), g, dim3(2 * fa::kThreads), 0, st, a);
     else if constexpr (sizeof(T) == 2 && D == 128)
       hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C>), g, b, 0, st, a);
     else

@@ -141,7 +141,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     ag[db] = aom[db] = ar[db] = abk[db] = zero16();
     asm volatile("" : "+a"(ag[db]), "+a"(aom[db]), "+a"(ar[db]), "+a"(abk[db]));
   }
-  float alpha_p = 0.0f, eo_p = 0.0f;
+  // eob_p: E° summed from the bf16-rounded products P t0 that the matrix core
+  // accumulates into Omega.  gQ = tau (Omega - alpha R' - E° B) uses it, so the
+  // rounded operands cancel the way the exact ones do (Sum_j (P t0 - E° P) = 0;
+  // on a row whose P sits on one key those terms cancel exactly).  E and the column
+  // pass keep the unrounded E°.
+  float alpha_p = 0.0f, eo_p = 0.0f, eob_p = 0.0f;
   // No load of the compiler's own may be outstanding inside the loop.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
@@ -213,9 +218,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float pf = p * F, pt = p * t0;
         alpha_p += pf;
         eo_p += pt;
+        const bf16 ptb = (bf16)pt;
+        eob_p += (float)ptb;
         cp.f[idx >> 3][idx & 7] = (bf16)p;
         cpf.f[idx >> 3][idx & 7] = (bf16)pf;
-        cpt.f[idx >> 3][idx & 7] = (bf16)pt;
+        cpt.f[idx >> 3][idx & 7] = ptb;
         cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
       }
     };
@@ -290,6 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   acc_fence<NDB>(ag, aom, ar, abk);
   const float alpha = half_sum(alpha_p);
   const float eo = half_sum(eo_p);
+  const float eob = half_sum(eob_p);
   if (row < N && hh == 0) {
     a.alpha[rv + row] = alpha;
     a.E[rv + row] = eo - alpha * Di;
@@ -323,7 +331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx] - alpha * ov[idx]; });
     store_out(gq, a.r0.sn, row, N, db,
-              [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eo * abk[db][idx]); });
+              [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eob * abk[db][idx]); });
   }
 }
 

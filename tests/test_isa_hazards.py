@@ -34,7 +34,29 @@ def test_library_assembly_has_no_mfma_hazards(tmp_path):
            "--cuda-device-only", "-S", "-I", build.INCLUDE, "-I", os.path.dirname(build.SRC), "-o", str(out), build.SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
-    found = check_asm(out.read_text())
-    assert any("bob_pass1_dma" in k for k in found) and any("bob_pass2_dma" in k for k in found)
+    text = out.read_text()
+    found = check_asm(text)
+    for name in ("bob_pass1_ws", "bob_pass1_dma", "bob_pass2_dma"):
+        assert any(name in k for k in found), name
     bad = {k: v for k, v in found.items() if v}
     assert not bad, {k: v[:5] for k, v in bad.items()}
+    # The bf16 BoB kernels keep everything in registers: a spill to scratch
+    # in their loops would be a silent slowdown.
+    spills = {k: n for k, n in scratch_sizes(text).items() if ("bob_pass1_ws" in k or "_dma_" in k) and n}
+    assert not spills, spills
+
+
+def scratch_sizes(text):
+    """Kernel symbol -> ScratchSize from the assembler's resource comments."""
+    import re
+
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            cur = m.group(1)
+        m = re.match(r"^; ScratchSize: (\d+)", line)
+        if m and cur:
+            out[cur] = int(m.group(1))
+            cur = None
+    return out
