@@ -13,6 +13,8 @@ Sources (cited by page title and section throughout):
   first backward), section 4.1 (the BoB functional Phi), section 4.2 (the
   closed-form outputs), appendix D (notation, reverse-mode Steps 1-7 and the
   final assembled identities).
+  Section 4.3 (the paragraph after Algorithm 1) for grouped-query and
+  multi-query attention (``gqa``).
 * [FA2-recompute] the interview answer "Why does FlashAttention-2's backward
   pass recompute attention, and what exactly does the forward pass save for
   it?": the saved state (O and one fp32 log-sum-exp per row) and the identity
@@ -25,6 +27,7 @@ memory.  Parity pins for every function live in ``tests/test_oracle_*.py``;
 none is "parity unpinned".
 """
 from .dense import backward_dense, bob_dense, forward_dense, phi_dense  # noqa: F401
+from .gqa import bob_dense_gqa, bob_streaming_gqa, col_pass_group  # noqa: F401
 from .streaming import (  # noqa: F401
     bob_streaming,
     col_pass,
