@@ -80,8 +80,9 @@ class Runner:
         self.fa, self.w = fa, w
         self.t = device_inputs(w)
         shape = (w.B, w.H, w.N, w.d)
+        kshape = (w.B, w.Hkv, w.N, w.d)  # key-side outputs: one per key/value head
         self.o, self.lse = fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], causal=w.causal)
-        self.outs = [torch.empty(shape, dtype=torch.float32, device="cuda") for _ in range(4)]
+        self.outs = [torch.empty(s, dtype=torch.float32, device="cuda") for s in (shape, kshape, kshape, shape)]
         code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP32
         self.ws = torch.empty(fa.bob_workspace_bytes(*shape, code, w.causal) // 4, dtype=torch.float32,
                               device="cuda")
@@ -175,7 +176,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mid")
-    ap.add_argument("--sweep", default="hd128,long,max,gpt2c_4k,gpt2c_16k,c128_16k",
+    ap.add_argument("--sweep", default="hd128,long,max,gpt2c_4k,gpt2c_16k,c128_16k,mqa_32k",
                     help="comma list of extra workloads ('' for none)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
@@ -224,7 +225,8 @@ def main():
         reps = 3 if sw.N >= 65536 or sw.bob_flops > 5e13 else 10
         _, s_ev, s_per = time_steps(r, reps, 1)
         tf = sw.bob_flops / (s_ev * 1e9)
-        sweep[name] = {"B": sw.B, "H": sw.H, "N": sw.N, "d": sw.d, "causal": sw.causal, "ms": round(s_ev, 3),
+        sweep[name] = {"B": sw.B, "H": sw.H, "H_kv": sw.Hkv, "N": sw.N, "d": sw.d, "causal": sw.causal,
+                       "ms": round(s_ev, 3),
                        "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                        "pass1_ms": round(s_per[1], 3), "pass2_ms": round(s_per[2], 3),
                        "rowscalar_ms": round(s_per[0], 4)}

@@ -42,7 +42,7 @@ class FaError(RuntimeError):
 class FaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d", ctypes.c_int64), ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int32)]
+                ("in_dtype", ctypes.c_int32), ("H_kv", ctypes.c_int64)]
 
 
 class FaTensor(ctypes.Structure):
@@ -100,9 +100,10 @@ def _torch():
     return torch
 
 
-def problem(B, H, N, d, in_dtype=FA_BF16, scale=None, causal=0) -> FaProblem:
+def problem(B, H, N, d, in_dtype=FA_BF16, scale=None, causal=0, H_kv=0) -> FaProblem:
+    """H: query heads; H_kv: key/value heads (0 = H; otherwise a divisor of H)."""
     return FaProblem(int(B), int(H), int(N), int(d), float(-1.0 if scale is None else scale),
-                     int(causal), int(in_dtype))
+                     int(causal), int(in_dtype), int(H_kv))
 
 
 def tensor_arg(t) -> FaTensor:
@@ -123,14 +124,23 @@ def _dtype_code(t):
     raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
 
 
-def _check_inputs(*ts):
-    first = ts[0]
-    for t in ts:
-        if t.shape != first.shape or t.dtype != first.dtype or t.device != first.device:
-            raise ValueError("q, k, v, dout and the cotangents must share shape, dtype and device")
-        if not t.is_cuda:
-            raise ValueError("tensors must live on the GPU")
-    return first.shape
+def _check_inputs(qside, kside):
+    """Query-side tensors [B, H, N, d] and key-side tensors [B, H_kv, N, d]
+    (H_kv dividing H) of one dtype on one device; returns (B, H, N, d, H_kv)."""
+    q0, k0 = qside[0], kside[0]
+    for group, ref in ((qside, q0), (kside, k0)):
+        for t in group:
+            if t.shape != ref.shape or t.dtype != q0.dtype or t.device != q0.device:
+                raise ValueError("q, dout and U_Q (and k, v, U_K, U_V) must share shape; all inputs share "
+                                 "dtype and device")
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+    B, H, N, d = q0.shape
+    Bk, Hkv, Nk, dk = k0.shape
+    if (Bk, Nk, dk) != (B, N, d) or Hkv < 1 or H % Hkv:
+        raise ValueError(f"key-side shape {tuple(k0.shape)} does not match query-side shape {tuple(q0.shape)} "
+                         "(same B, N, d; key/value heads must divide query heads)")
+    return B, H, N, d, Hkv
 
 
 def _stream(stream):
@@ -158,10 +168,11 @@ def _call(name, status):
 
 def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, causal=False):
     """Forward: returns (O fp32 [B,H,N,d], L fp32 [B,H,N], natural-log
-    log-sum-exp of tau q.k over the (causally) valid keys)."""
+    log-sum-exp of tau q.k over the (causally) valid keys).  k, v may have
+    fewer heads than q (grouped-query / multi-query attention)."""
     torch = _torch()
-    B, H, N, d = _check_inputs(q, k, v)
-    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)))
+    B, H, N, d, Hkv = _check_inputs((q,), (k, v))
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
     o = _f32_like(q, o)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -191,10 +202,11 @@ def _workspace(nbytes, device, ws):
 
 def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None, stream=None,
            causal=False):
-    """First backward: returns (dQ, dK, dV) fp32 and the workspace holding D."""
-    B, H, N, d = _check_inputs(q, k, v, dout)
-    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)))
-    dq, dk, dv = _f32_like(q, dq), _f32_like(q, dk), _f32_like(q, dv)
+    """First backward: returns (dQ, dK, dV) fp32 and the workspace holding D.
+    dK, dV have k's heads (sums over each group's query heads)."""
+    B, H, N, d, Hkv = _check_inputs((q, dout), (k, v))
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
+    dq, dk, dv = _f32_like(q, dq), _f32_like(k, dk), _f32_like(k, dv)
     nbytes = int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
     ws = _workspace(nbytes, q.device, ws)
     _call("fa_bwd", load_library().fa_bwd(
@@ -208,12 +220,14 @@ def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None
 def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=None, gdo=None,
            ws=None, stream=None, phase=None, causal=False):
     """Backward-over-backward: gradients of <dQ,U_Q> + <dK,U_K> + <dV,U_V> with
-    respect to Q, K, V and dO.  Returns (gQ, gK, gV, gdO, ws) with
+    respect to Q, K, V and dO (k, v, uk, uv and gK, gV may have fewer heads
+    than q: grouped-query / multi-query attention).  Returns (gQ, gK, gV, gdO, ws) with
     ws = [D | alpha | E], each [B, H, N] fp32.  ``phase`` (0, 1 or 2) calls
     fa_bob_phase instead, launching only that kernel."""
-    B, H, N, d = _check_inputs(q, k, v, dout, uq, uk, uv)
-    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)))
-    gq, gk, gv, gdo = (_f32_like(q, x) for x in (gq, gk, gv, gdo))
+    B, H, N, d, Hkv = _check_inputs((q, dout, uq), (k, v, uk, uv))
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
+    gq, gdo = _f32_like(q, gq), _f32_like(q, gdo)
+    gk, gv = _f32_like(k, gk), _f32_like(k, gv)
     lib = load_library()
     nbytes = int(lib.fa_bob_workspace_bytes(ctypes.byref(p)))
     ws = _workspace(nbytes, q.device, ws)

@@ -18,6 +18,7 @@ constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
 
 struct Ctx {
   int64_t B, H, N, d;
+  int64_t Hkv, G;  // key/value heads, query heads per key/value head
   size_t esize;  // input element size
   bool bf;
   bool causal;
@@ -27,6 +28,8 @@ struct Ctx {
 fa_status check_problem(const fa_problem* p, Ctx* c) {
   if (!p) return FA_ERR_NULL;
   if (p->B < 1 || p->H < 1 || p->N < 1) return FA_ERR_SHAPE;
+  const int64_t hkv = p->H_kv == 0 ? p->H : p->H_kv;
+  if (hkv < 1 || hkv > p->H || p->H % hkv) return FA_ERR_SHAPE;
   if (p->in_dtype != FA_BF16 && p->in_dtype != FA_FP32) return FA_ERR_DTYPE;
   if (p->d != 64 && p->d != 128) return FA_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return FA_ERR_UNSUPPORTED;
@@ -50,6 +53,8 @@ fa_status check_problem(const fa_problem* p, Ctx* c) {
   const float m = frexpf(tau, &ex);  // tau = m * 2^ex, m in [0.5, 1)
   c->B = p->B;
   c->H = p->H;
+  c->Hkv = hkv;
+  c->G = p->H / hkv;
   c->N = p->N;
   c->d = p->d;
   c->bf = p->in_dtype == FA_BF16;
@@ -93,6 +98,8 @@ Args base_args(const Ctx& c) {
   memset(&a, 0, sizeof(a));
   a.B = (int)c.B;
   a.H = (int)c.H;
+  a.Hk = (int)c.Hkv;
+  a.G = (int)c.G;
   a.N = (int)c.N;
   a.tau = c.tau;
   a.pow2 = c.pow2;
@@ -103,6 +110,12 @@ Args base_args(const Ctx& c) {
 
 unsigned grid_rows(const Ctx& c) {
   return (unsigned)(c.B * c.H * ((c.N + fa::kResRows - 1) / fa::kResRows));
+}
+
+// Column-side kernels: one workgroup per (batch, key/value head, key block);
+// each streams the rows of the group's G query heads.
+unsigned grid_cols(const Ctx& c) {
+  return (unsigned)(c.B * c.Hkv * ((c.N + fa::kResRows - 1) / fa::kResRows));
 }
 
 unsigned grid_rowscalar(const Ctx& c) {
@@ -140,7 +153,7 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
   launch_rowscalar<T, D>(c, a, st);
   hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
                      a);
-  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
+  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0,
                      st, a);
 }
 
@@ -159,12 +172,13 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
       hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
   }
   if (phase < 0 || phase == 2) {
+    const dim3 gc(grid_cols(c));
     if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), g, b, 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), gc, b, 0, st, a);
     else if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), g, b, 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), gc, b, 0, st, a);
     else
-      hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
+      hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), gc, b, 0, st, a);
   }
 }
 

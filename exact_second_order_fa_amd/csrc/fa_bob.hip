@@ -108,8 +108,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
   const HeadPtr<bf16> q = head_of<bf16>(a.q, wk.b, wk.h), uq = head_of<bf16>(a.uq, wk.b, wk.h),
                       dout = head_of<bf16>(a.dout, wk.b, wk.h);
-  HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, wk.b, wk.h), head_of<bf16>(a.v, wk.b, wk.h),
-                          head_of<bf16>(a.uk, wk.b, wk.h), head_of<bf16>(a.uv, wk.b, wk.h)};
+  HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, wk.b, wk.hk), head_of<bf16>(a.v, wk.b, wk.hk),
+                          head_of<bf16>(a.uk, wk.b, wk.hk), head_of<bf16>(a.uv, wk.b, wk.hk)};
   const int nt = (N + TS - 1) / TS;
   // Causal: key tiles past this row block's last row are skipped, and the
   // tiles from t_diag on cross the diagonal and are masked element by element.
@@ -358,37 +358,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(kPsRows % TS == 0 && (TS == 64 || TS == 128), "tiles split the staged scalar blocks");
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item_cols(a);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
-  const HeadPtr<bf16> k = head_of<bf16>(a.k, wk.b, wk.h), v = head_of<bf16>(a.v, wk.b, wk.h),
-                      uk = head_of<bf16>(a.uk, wk.b, wk.h), uv = head_of<bf16>(a.uv, wk.b, wk.h);
+  const HeadPtr<bf16> k = head_of<bf16>(a.k, wk.b, wk.hk), v = head_of<bf16>(a.v, wk.b, wk.hk),
+                      uk = head_of<bf16>(a.uk, wk.b, wk.hk), uv = head_of<bf16>(a.uv, wk.b, wk.hk);
+  // Streamed: the G query heads of this key/value head in sequence (the
+  // key-side outputs sum over the group, [FlashBoB] section 4.3).
   HeadPtr<bf16> src[3] = {head_of<bf16>(a.q, wk.b, wk.h), head_of<bf16>(a.dout, wk.b, wk.h),
                           head_of<bf16>(a.uq, wk.b, wk.h)};
+  const int64_t hstride[3] = {a.q.sh, a.dout.sh, a.uq.sh};
   const int nt = (N + TS - 1) / TS;
-  const float* psh = a.ps + (int64_t)wk.bh * ((N + kPsRows - 1) / kPsRows) * 4 * kPsRows;
+  const int64_t ps_head = (int64_t)((N + kPsRows - 1) / kPsRows) * 4 * kPsRows;  // floats per query head
+  const float* ps0 = a.ps + ((int64_t)wk.b * a.H + wk.h) * ps_head;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   Dma<D, TS, 3> dma;
-  dma.init(src);
-  auto copy_tile = [&](int t, const char* dst) {
-    dma.copy(t * TS, N, dst);
+  dma.init(src, hstride);
+  // Tile t of query head h + g into dst.
+  auto copy_tile = [&](int g, int t, const char* dst) {
+    dma.copy(t * TS, N, dst, g);
     // The tile's chain inits, [4][TS] floats: TS / 64 wave-wide copies.  Lane l
     // of copy w moves rows 4 (l % 16) .. +3 of init (4 w + l / 16) % 4 ...
     if (wave < SBYTES / 1024) {
       const int r0 = t * TS;
       const int e = (wave * 64 + l) * 4;  // float index inside the [4][TS] block
       const int kk = e / TS, rr = e % TS;
-      const float* g = psh + ((int64_t)(r0 / kPsRows) * 4 + kk) * kPsRows + r0 % kPsRows + rr;
-      dma16(g, lds_addr(dst + TBYTES + wave * 1024));
+      const float* src_ps = ps0 + g * ps_head + ((int64_t)(r0 / kPsRows) * 4 + kk) * kPsRows + r0 % kPsRows + rr;
+      dma16(src_ps, lds_addr(dst + TBYTES + wave * 1024));
     }
   };
   // Causal: query tiles before this key block's first key are skipped; tiles
   // below t_diag cross the diagonal and are masked element by element.
   const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
   const int t_diag = CAUSAL ? (wk.rb * kResRows + kResRows + TS - 1) / TS : 0;
-  copy_tile(t_begin, lds + (t_begin & 1) * STAGE);
+  copy_tile(0, t_begin, lds);
 
   bf16x8 kf[NKS], ukf[NKS], vf[NKS], uvf[NKS];
   load_resident<bf16, D>(kf, k.p, k.sn, col, N, a.pow2);
@@ -414,9 +419,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // Tile modes: 0 = rows masked only through the staged inits, 2 = causal
   // diagonal tile (also -inf where query < key).
-  auto tile_body = [&](int t, auto mode_c) {
+  // Tile t in LDS buffer buf.
+  auto tile_body = [&](int t, int buf, auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
-    const char* tq = lds + (t & 1) * STAGE;
+    const char* tq = lds + buf * STAGE;
     const char* tdo = tq + W::BYTES;
     const char* tuq = tq + 2 * W::BYTES;
     const float* sc = reinterpret_cast<const float*>(tq + TBYTES);
@@ -513,21 +519,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  auto run = [&](int t0, int t1, auto mode_c) {
-    for (int t = t0; t < t1; ++t) {
-      dma_wait();
-      __syncthreads();
-      if (t + 1 < nt) copy_tile(t + 1, lds + ((t + 1) & 1) * STAGE);
-      tile_body(t, mode_c);
-    }
-    acc_fence2<NDB>(ak, av);
-  };
-  if constexpr (CAUSAL) run(t_begin, min(t_diag, nt), std::integral_constant<int, 2>{});
-  run(CAUSAL ? min(t_diag, nt) : 0, nt, std::integral_constant<int, 0>{});
+  // u counts the tiles of all heads (it picks the LDS buffer); the copy of
+  // the next tile, possibly the next head's first, overlaps the current one.
+  int u = 0;
+  for (int g = 0; g < a.G; ++g) {
+    auto run = [&](int t0, int t1, auto mode_c) {
+      for (int t = t0; t < t1; ++t) {
+        dma_wait();
+        __syncthreads();
+        const char* next = lds + ((u + 1) & 1) * STAGE;
+        if (t + 1 < nt) {
+          copy_tile(g, t + 1, next);
+        } else if (g + 1 < a.G) {
+          copy_tile(g + 1, t_begin, next);
+        }
+        tile_body(t, u & 1, mode_c);
+        ++u;
+      }
+      acc_fence2<NDB>(ak, av);
+    };
+    if constexpr (CAUSAL) run(t_begin, min(t_diag, nt), std::integral_constant<int, 2>{});
+    run(CAUSAL ? min(t_diag, nt) : 0, nt, std::integral_constant<int, 0>{});
+  }
 
   acc_fence2<NDB>(ak, av);
-  float* gk = head_out(a.r1, wk.b, wk.h);
-  float* gv = head_out(a.r2, wk.b, wk.h);
+  float* gk = head_out(a.r1, wk.b, wk.hk);
+  float* gv = head_out(a.r2, wk.b, wk.hk);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     store_out(gk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });

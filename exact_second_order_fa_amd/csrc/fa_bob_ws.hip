@@ -134,7 +134,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int nblk = (a.N + kResRows - 1) / kResRows;
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wid / nblk, rb = wid % nblk, bb = bh / a.H, hd = bh % a.H;
+  const int bh = wid / nblk, rb = wid % nblk, bb = bh / a.H, hd = bh % a.H, hk = hd / a.G;
   const int N = a.N;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool producer = wave < 4;
@@ -143,8 +143,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int r0 = rb * kResRows;
   const int row = r0 + wi * 32 + (l & 31);
 
-  HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, bb, hd), head_of<bf16>(a.v, bb, hd), head_of<bf16>(a.uk, bb, hd),
-                          head_of<bf16>(a.uv, bb, hd)};
+  HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, bb, hk), head_of<bf16>(a.v, bb, hk), head_of<bf16>(a.uk, bb, hk),
+                          head_of<bf16>(a.uv, bb, hk)};
   const int nt = CAUSAL ? min((N + TS - 1) / TS, (r0 + kResRows) / TS) : (N + TS - 1) / TS;
   WsDma dma;
   dma.init(src);

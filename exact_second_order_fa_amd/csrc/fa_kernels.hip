@@ -35,6 +35,7 @@ struct Args {
   float* E;                            // [B,H,N] BoB row scalar E
   float* ps;                           // [B*H][ceil(N/128)][4][128] column-pass chain inits
   int B, H, N;
+  int Hk, G;                 // key/value heads and query heads per key/value head (H = Hk * G)
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
 };
 
@@ -50,8 +51,15 @@ __device__ inline float* head_out(const TDesc& t, int b, int h) {
   return reinterpret_cast<float*>(const_cast<void*>(t.p)) + (int64_t)b * t.sb + (int64_t)h * t.sh;
 }
 
+// One workgroup's share: batch b, row block rb and
+//   * row-side kernels (a block of query rows): query head h, bh = b * H + h,
+//     and the key/value head hk = h / G its keys come from;
+//   * column-side kernels (a block of key rows): key/value head hk,
+//     bh = b * Hk + hk; its G query heads are hk * G .. hk * G + G - 1, the
+//     first of them in h ([FlashBoB] section 4.3: the key-side outputs sum
+//     over the group inside one workgroup).
 struct Work {
-  int bh, b, h, rb;
+  int bh, b, h, hk, rb;
 };
 
 __device__ inline Work work_item(const Args& a) {
@@ -62,6 +70,19 @@ __device__ inline Work work_item(const Args& a) {
   r.rb = w % nblk;
   r.b = r.bh / a.H;
   r.h = r.bh % a.H;
+  r.hk = r.h / a.G;
+  return r;
+}
+
+__device__ inline Work work_item_cols(const Args& a) {
+  const int nblk = (a.N + kResRows - 1) / kResRows;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  Work r;
+  r.bh = w / nblk;
+  r.rb = w % nblk;
+  r.b = r.bh / a.Hk;
+  r.hk = r.bh % a.Hk;
+  r.h = r.hk * a.G;
   return r;
 }
 
@@ -198,7 +219,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
   const HeadPtr<T> q = head_of<T>(a.q, wk.b, wk.h);
-  HeadPtr<T> src[2] = {head_of<T>(a.k, wk.b, wk.h), head_of<T>(a.v, wk.b, wk.h)};
+  HeadPtr<T> src[2] = {head_of<T>(a.k, wk.b, wk.hk), head_of<T>(a.v, wk.b, wk.hk)};
 
   typename E::frag qf[NKS];
   load_resident<T, D>(qf, q.p, q.sn, row, N, a.pow2);
@@ -290,7 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
   const HeadPtr<T> q = head_of<T>(a.q, wk.b, wk.h), dout = head_of<T>(a.dout, wk.b, wk.h);
-  HeadPtr<T> src[2] = {head_of<T>(a.k, wk.b, wk.h), head_of<T>(a.v, wk.b, wk.h)};
+  HeadPtr<T> src[2] = {head_of<T>(a.k, wk.b, wk.hk), head_of<T>(a.v, wk.b, wk.hk)};
 
   typename E::frag qf[NKS], df[NKS];
   load_resident<T, D>(qf, q.p, q.sn, row, N, a.pow2);
@@ -363,17 +384,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float scl[2][2 * TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item_cols(a);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
-  const HeadPtr<T> k = head_of<T>(a.k, wk.b, wk.h), v = head_of<T>(a.v, wk.b, wk.h);
-  HeadPtr<T> src[2] = {head_of<T>(a.q, wk.b, wk.h), head_of<T>(a.dout, wk.b, wk.h)};
+  const HeadPtr<T> k = head_of<T>(a.k, wk.b, wk.hk), v = head_of<T>(a.v, wk.b, wk.hk);
+  HeadPtr<T> src[2];
 
   typename E::frag kf[NKS], vf[NKS];
   load_resident<T, D>(kf, k.p, k.sn, col, N, a.pow2);
   load_resident<T, D>(vf, v.p, v.sn, col, N, 1.0f);
-  const int64_t rv = (int64_t)wk.bh * N;
+  int64_t rv = 0;  // row-vector base of the query head being staged
   const float irho = 1.0f / a.rho;
   auto scal = [&](int row, float* o) {
     o[0] = -a.lse[rv + row] * irho;
@@ -390,23 +411,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 2> st;
   ScalarStager<TS, 2> ss;
+  // Row tiles of the G query heads of this key/value head in sequence, all
+  // into the same accumulators: tile u is row tile t_begin + u % ntq of query
+  // head h + u / ntq.
   const int nt = (N + TS - 1) / TS;
   const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
-  st.load(src, t_begin * TS, N);
-  ss.load(t_begin * TS, N, scal, pad);
-  st.store(lds[t_begin & 1]);
-  ss.store(scl[t_begin & 1]);
+  const int ntq = nt - t_begin, nu = a.G * ntq;
+  auto load_tile = [&](int u) {
+    const int hq = wk.h + u / ntq, t = t_begin + u % ntq;
+    src[0] = head_of<T>(a.q, wk.b, hq);
+    src[1] = head_of<T>(a.dout, wk.b, hq);
+    rv = ((int64_t)wk.b * a.H + hq) * N;
+    st.load(src, t * TS, N);
+    ss.load(t * TS, N, scal, pad);
+  };
+  load_tile(0);
+  st.store(lds[0]);
+  ss.store(scl[0]);
   __syncthreads();
-  for (int t = t_begin; t < nt; ++t) {
-    if (t + 1 < nt) {
-      st.load(src, (t + 1) * TS, N);
-      ss.load((t + 1) * TS, N, scal, pad);
-    }
-    const T* qr = lds[t & 1];
+  for (int u = 0; u < nu; ++u) {
+    const int t = t_begin + u % ntq;
+    if (u + 1 < nu) load_tile(u + 1);
+    const T* qr = lds[u & 1];
     const T* qt = qr + S::ROW_ELEMS;
     const T* dr = qr + S::ELEMS;
     const T* dt = dr + S::ROW_ELEMS;
-    const float* sc = scl[t & 1];
+    const float* sc = scl[u & 1];
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
@@ -429,14 +459,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           ak[db] = E::mma(tr_frag<T, D, TS>(qt, db, sub, s2), cds.f[s2], ak[db]);
         }
     }
-    if (t + 1 < nt) {
-      st.store(lds[(t + 1) & 1]);
-      ss.store(scl[(t + 1) & 1]);
+    if (u + 1 < nu) {
+      st.store(lds[(u + 1) & 1]);
+      ss.store(scl[(u + 1) & 1]);
     }
     __syncthreads();
   }
-  float* dk = head_out(a.r1, wk.b, wk.h);
-  float* dv = head_out(a.r2, wk.b, wk.h);
+  float* dk = head_out(a.r1, wk.b, wk.hk);
+  float* dv = head_out(a.r2, wk.b, wk.hk);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     store_out(dk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
@@ -474,8 +504,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
   const HeadPtr<T> q = head_of<T>(a.q, wk.b, wk.h), uq = head_of<T>(a.uq, wk.b, wk.h),
                    dout = head_of<T>(a.dout, wk.b, wk.h);
-  HeadPtr<T> src[4] = {head_of<T>(a.k, wk.b, wk.h), head_of<T>(a.v, wk.b, wk.h), head_of<T>(a.uk, wk.b, wk.h),
-                       head_of<T>(a.uv, wk.b, wk.h)};
+  HeadPtr<T> src[4] = {head_of<T>(a.k, wk.b, wk.hk), head_of<T>(a.v, wk.b, wk.hk), head_of<T>(a.uk, wk.b, wk.hk),
+                       head_of<T>(a.uv, wk.b, wk.hk)};
 
   typename E::frag qf[NKS], uqf[NKS], df[NKS];
   load_resident<T, D>(qf, q.p, q.sn, row, N, a.pow2);
@@ -611,20 +641,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][3 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float scl[2][4 * TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item_cols(a);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
-  const HeadPtr<T> k = head_of<T>(a.k, wk.b, wk.h), v = head_of<T>(a.v, wk.b, wk.h),
-                   uk = head_of<T>(a.uk, wk.b, wk.h), uv = head_of<T>(a.uv, wk.b, wk.h);
-  HeadPtr<T> src[3] = {head_of<T>(a.q, wk.b, wk.h), head_of<T>(a.dout, wk.b, wk.h), head_of<T>(a.uq, wk.b, wk.h)};
+  const HeadPtr<T> k = head_of<T>(a.k, wk.b, wk.hk), v = head_of<T>(a.v, wk.b, wk.hk),
+                   uk = head_of<T>(a.uk, wk.b, wk.hk), uv = head_of<T>(a.uv, wk.b, wk.hk);
+  HeadPtr<T> src[3];
 
   typename E::frag kf[NKS], vf[NKS], ukf[NKS], uvf[NKS];
   load_resident<T, D>(kf, k.p, k.sn, col, N, a.pow2);
   load_resident<T, D>(ukf, uk.p, uk.sn, col, N, a.pow2);
   load_resident<T, D>(vf, v.p, v.sn, col, N, 1.0f);
   load_resident<T, D>(uvf, uv.p, uv.sn, col, N, 1.0f);
-  const int64_t rv = (int64_t)wk.bh * N;
+  int64_t rv = 0;  // row-vector base of the query head being staged
   const float irho = 1.0f / a.rho;
   auto scal = [&](int row, float* o) {
     const float L = a.lse[rv + row], Dd = a.D[rv + row], al = a.alpha[rv + row], Ee = a.E[rv + row];
@@ -644,25 +674,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   Stager<T, D, TS, 3> st;
   ScalarStager<TS, 4> ss;
+  // Row tiles of the G query heads of this key/value head in sequence (see
+  // bwd_dkdv_kernel).
   const int nt = (N + TS - 1) / TS;
   const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
-  st.load(src, t_begin * TS, N);
-  ss.load(t_begin * TS, N, scal, pad);
-  st.store(lds[t_begin & 1]);
-  ss.store(scl[t_begin & 1]);
+  const int ntq = nt - t_begin, nu = a.G * ntq;
+  auto load_tile = [&](int u) {
+    const int hq = wk.h + u / ntq, t = t_begin + u % ntq;
+    src[0] = head_of<T>(a.q, wk.b, hq);
+    src[1] = head_of<T>(a.dout, wk.b, hq);
+    src[2] = head_of<T>(a.uq, wk.b, hq);
+    rv = ((int64_t)wk.b * a.H + hq) * N;
+    st.load(src, t * TS, N);
+    ss.load(t * TS, N, scal, pad);
+  };
+  load_tile(0);
+  st.store(lds[0]);
+  ss.store(scl[0]);
   __syncthreads();
-  for (int t = t_begin; t < nt; ++t) {
-    if (t + 1 < nt) {
-      st.load(src, (t + 1) * TS, N);
-      ss.load((t + 1) * TS, N, scal, pad);
-    }
-    const T* qr = lds[t & 1];
+  for (int u = 0; u < nu; ++u) {
+    const int t = t_begin + u % ntq;
+    if (u + 1 < nu) load_tile(u + 1);
+    const T* qr = lds[u & 1];
     const T* qt = qr + S::ROW_ELEMS;
     const T* dr = qr + S::ELEMS;
     const T* dt = dr + S::ROW_ELEMS;
     const T* uqr = qr + 2 * S::ELEMS;
     const T* uqt = uqr + S::ROW_ELEMS;
-    const float* sc = scl[t & 1];
+    const float* sc = scl[u & 1];
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
@@ -693,14 +732,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           av[db] = E::mma(tr_frag<T, D, TS>(dt, db, sub, s2), cw.f[s2], av[db]);
         }
     }
-    if (t + 1 < nt) {
-      st.store(lds[(t + 1) & 1]);
-      ss.store(scl[(t + 1) & 1]);
+    if (u + 1 < nu) {
+      st.store(lds[(u + 1) & 1]);
+      ss.store(scl[(u + 1) & 1]);
     }
     __syncthreads();
   }
-  float* gk = head_out(a.r1, wk.b, wk.h);
-  float* gv = head_out(a.r2, wk.b, wk.h);
+  float* gk = head_out(a.r1, wk.b, wk.hk);
+  float* gv = head_out(a.r2, wk.b, wk.hk);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
     store_out(gk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });

@@ -107,10 +107,13 @@ struct Dma {
 
   const char* base[NT];  // head base pointers (uniform)
   int64_t rs[NT];        // row strides in bytes (uniform)
+  int64_t hs[NT];        // head strides in bytes (uniform; copy() may step over heads)
   uint32_t off[NT];      // per-lane byte offset inside a block: jl * rs + 16 q
   int jl, wave;
 
-  __device__ inline void init(const HeadPtr<bf16>* src) {
+  // src: the tensors' first heads; hstride: their head strides in elements
+  // (needed only by copies with g != 0).
+  __device__ inline void init(const HeadPtr<bf16>* src, const int64_t* hstride = nullptr) {
     const int lane = lane_id();
     wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     jl = lane / W::G;
@@ -119,28 +122,31 @@ struct Dma {
     for (int t = 0; t < NT; ++t) {
       base[t] = reinterpret_cast<const char*>(src[t].p);
       rs[t] = src[t].sn * 2;
+      hs[t] = hstride ? hstride[t] * 2 : 0;
       off[t] = (uint32_t)(jl * (int)rs[t] + 16 * q);
     }
   }
 
-  __device__ inline void copy(int row0, int N, const char* dst) const {
+  // Rows row0 .. row0 + TS - 1 of head g (counted from the heads passed to
+  // init) of every tensor.
+  __device__ inline void copy(int row0, int N, const char* dst, int g = 0) const {
     const uint32_t lbase = lds_addr(dst);
-    const int lane = lane_id();
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+      const char* hb = base[t] + g * hs[t];
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int b = i * NW + wave;
         const int r0 = row0 + b * RPB;
         const uint32_t lds = lbase + t * W::BYTES + b * 1024;
         if (r0 + RPB <= N) {
-          dma16_so(base[t] + r0 * rs[t], off[t], lds);
+          dma16_so(hb + r0 * rs[t], off[t], lds);
         } else {
           const int row = min(r0 + jl, N - 1);
-          dma16(base[t] + row * rs[t] + (off[t] - jl * (int)rs[t]), lds);
+          dma16(hb + row * rs[t] + (off[t] - jl * (int)rs[t]), lds);
         }
-        (void)lane;
       }
+    }
   }
 };
 

@@ -10,7 +10,8 @@ Recipe (the same on every machine, since numpy's PCG64 stream is portable):
 
 * ``numpy.random.default_rng(seed)``;
 * ``standard_normal(size=(B, H, N, d), dtype=float32)`` drawn seven times in
-  the order Q, K, V, dO, U_Q, U_K, U_V;
+  the order Q, K, V, dO, U_Q, U_K, U_V (with grouped-query / multi-query
+  attention K, V, U_K, U_V are drawn with H_kv heads instead of H);
 * workload scalings (cotangent standard deviation, a Q/K gain that peaks the
   softmax rows);
 * for bf16 workloads, round-to-nearest-even to bfloat16.  The GPU receives

@@ -22,7 +22,12 @@ class Workload:
     cot_std: float = 1.0  # standard deviation of U_Q, U_K, U_V
     qk_gain: float = 1.0  # extra factor on Q and K rows (peaked softmax rows)
     causal: bool = False
+    H_kv: int = 0  # key/value heads (0: same as H); grouped-query / multi-query below H
     note: str = field(default="", compare=False)
+
+    @property
+    def Hkv(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def scale(self) -> float:
@@ -41,6 +46,8 @@ class Workload:
         """
         f = 38.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
+    # With grouped-query attention the count is per query head: every query
+    # head's rows meet every key of its group's head in both passes.
 
 
 WORKLOADS = {
@@ -55,6 +62,9 @@ WORKLOADS = {
     "gpt2c_4k": Workload("gpt2c_4k", 4, 12, 4096, 64, "bf16", 5, causal=True),
     "gpt2c_16k": Workload("gpt2c_16k", 4, 12, 16384, 64, "bf16", 6, causal=True),
     "c128_16k": Workload("c128_16k", 4, 12, 16384, 128, "bf16", 7, causal=True),
+    # The pages' multi-query benchmark shape (H_Q / H_KV = 8 / 1, batch 1,
+    # N from 2K to 128K); no mask or input distribution is stated for it.
+    "mqa_32k": Workload("mqa_32k", 1, 8, 32768, 64, "bf16", 8, H_kv=1),
 }
 
 
@@ -78,8 +88,9 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
-                cot_std: float = 1.0, qk_gain: float = 1.0, with_f64: bool = True):
-    """Draw the seven inputs.
+                cot_std: float = 1.0, qk_gain: float = 1.0, with_f64: bool = True, H_kv: int = 0):
+    """Draw the seven inputs, in the order of NAMES: q, do, uq with shape
+    (B, H, N, d); k, v, uk, uv with shape (B, H_kv, N, d) (H_kv = 0: H).
 
     Returns ``(raw, f64)``: ``raw`` maps each name to the array the device
     receives (uint16 bf16 bits, or float32), ``f64`` maps each name to the
@@ -89,9 +100,13 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
     if dtype not in ("bf16", "fp32"):
         raise ValueError(f"unknown dtype {dtype!r}")
     rng = np.random.default_rng(seed)
+    Hk = H_kv or H
+    if H % Hk:
+        raise ValueError(f"H_kv = {Hk} does not divide H = {H}")
     raw, f64 = {}, {}
     for name in NAMES:
-        x = rng.standard_normal(size=(B, H, N, d), dtype=np.float32)
+        heads = Hk if name in ("k", "v", "uk", "uv") else H
+        x = rng.standard_normal(size=(B, heads, N, d), dtype=np.float32)
         if name in ("uq", "uk", "uv") and cot_std != 1.0:
             x = (x * np.float32(cot_std)).astype(np.float32)
         if name in ("q", "k") and qk_gain != 1.0:
@@ -109,4 +124,4 @@ def make_inputs(B: int, H: int, N: int, d: int, seed: int, dtype: str = "bf16",
 def workload_inputs(w: Workload, N: int | None = None, with_f64: bool = True):
     """Inputs of a named workload (optionally with a different length N)."""
     return make_inputs(w.B, w.H, w.N if N is None else N, w.d, w.seed, w.dtype,
-                       w.cot_std, w.qk_gain, with_f64)
+                       w.cot_std, w.qk_gain, with_f64, w.H_kv)

@@ -12,11 +12,19 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Problem: B batches x H heads, sequence length N (queries = keys), head
- * dimension d, softmax scale tau, full or causal attention.  Causal adds the
- * mask term B_mask = -inf for key j > query i to S ([FlashBoB] section 3);
+ * Problem: B batches x H query heads, sequence length N (queries = keys),
+ * head dimension d, softmax scale tau, full or causal attention.  Causal adds
+ * the mask term B_mask = -inf for key j > query i to S ([FlashBoB] section 3);
  * key tiles entirely above the diagonal are skipped.  One attention head is
  * the (b, h) slice.
+ *
+ * Grouped-query / multi-query attention ([FlashBoB] section 4.3, the
+ * paragraph after Algorithm 1): H_kv key/value heads, H_kv dividing H, G =
+ * H / H_kv.  Query head h attends to key/value head h / G (consecutive query
+ * heads share a head).  K, V, U_K, U_V and the key-side outputs dK, dV, gK,
+ * gV have H_kv heads; every key-side output is the sum over its group's G
+ * query heads, accumulated inside one workgroup (no atomics).  H_kv = 0 or
+ * H_kv = H is multi-head attention.
  *
  * Tensors: every N x d operand is passed as an fa_tensor: a DEVICE pointer
  * plus element strides for the batch, head and sequence dimensions; the head
@@ -53,7 +61,7 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,        /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,       /* B, H or N < 1, or sizes overflow */
+  FA_ERR_SHAPE = 2,       /* B, H or N < 1, H_kv not 0 or a divisor of H, or sizes overflow */
   FA_ERR_STRIDE = 3,      /* stride or alignment rule violated */
   FA_ERR_DTYPE = 4,       /* unknown input dtype */
   FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128}, causal not 0/1, or a non-finite/negative scale */
@@ -71,6 +79,7 @@ typedef struct fa_problem {
   float scale;      /* tau; a value <= 0 selects 1/sqrt(d) */
   int32_t causal;   /* 0: full attention; 1: causal (key j > query i masked) */
   int32_t in_dtype; /* an fa_dtype */
+  int64_t H_kv;     /* key/value heads: 0 (= H) or a divisor of H */
 } fa_problem;
 
 typedef struct fa_tensor {
@@ -107,7 +116,8 @@ size_t fa_bwd_workspace_bytes(const fa_problem* p);
  * with D_i = rowsum(dO * O)_i ([FA2-recompute]), computed by a row-scalar
  * kernel into the workspace (first B*H*N floats).
  * In:  q, k, v, dout (in_dtype); o (fp32) and lse (fp32) from fa_fwd.
- * Out: dq, dk, dv (fp32).  Deterministic: every output block has one writer.
+ * Out: dq (H heads), dk, dv (H_kv heads: sums over each group) in fp32.
+ * Deterministic: every output block has one writer.
  */
 fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor o, const float* lse, fa_tensor dout,
@@ -136,8 +146,9 @@ size_t fa_bob_workspace_bytes(const fa_problem* p);
  * section 4.2 and writes gq, gdo, alpha, E once per row block; a
  * column-major pass writes gk, gv once per column block.  No N x N tensor is
  * written anywhere and no atomics are used, so results are deterministic.
- * In:  q, k, v, dout, uq, uk, uv (in_dtype); o (fp32), lse (fp32) from fa_fwd.
- * Out: gq, gk, gv, gdo (fp32).  Workspace: [D | alpha | E | internal], D,
+ * In:  q, k, v, dout, uq, uk, uv (in_dtype); o (fp32), lse (fp32) from fa_fwd;
+ *      k, v, uk, uv have H_kv heads.
+ * Out: gq, gdo (H heads), gk, gv (H_kv heads) in fp32.  Workspace: [D | alpha | E | internal], D,
  *      alpha, E each contiguous [B,H,N] fp32 (this part of the layout is part
  *      of the ABI); the internal tail carries per-row values from the row pass
  *      to the column pass.

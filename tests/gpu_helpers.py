@@ -56,10 +56,10 @@ def run_path(t, scale=None, with_bwd=True, layout="bhnd", causal=False):
     res = {"O": o, "L": lse}
     if with_bwd:
         dq, dk, dv, _ = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], scale=scale,
-                                  dq=empty_like_out(t["q"]), dk=empty_like_out(t["q"]),
-                                  dv=empty_like_out(t["q"]), causal=causal)
+                                  dq=empty_like_out(t["q"]), dk=empty_like_out(t["k"]),
+                                  dv=empty_like_out(t["k"]), causal=causal)
         res.update(dQ=dq, dK=dk, dV=dv)
-    outs = [empty_like_out(t["q"]) for _ in range(4)]
+    outs = [empty_like_out(t[n]) for n in ("q", "k", "k", "q")]  # gQ, gK, gV, gdO
     gq, gk, gv, gdo, ws = fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"],
                                     scale=scale, gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3],
                                     causal=causal)

@@ -47,12 +47,36 @@ def test_version_and_status_strings(lib):
     assert lib.fa_status_str(99).decode() == "unknown status"
 
 
-def prob(B=1, H=2, N=100, d=64, scale=-1.0, causal=0, dt=fa.FA_BF16):
-    return FaProblem(B, H, N, d, scale, causal, dt)
+def prob(B=1, H=2, N=100, d=64, scale=-1.0, causal=0, dt=fa.FA_BF16, Hkv=0):
+    return FaProblem(B, H, N, d, scale, causal, dt, Hkv)
+
+
+def test_problem_struct_layout(tmp_path):
+    """The ctypes mirror of fa_problem and fa_tensor matches include/fa.h as a C
+    compiler lays it out."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fa.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(fa_problem), '
+                   'offsetof(fa_problem, scale), offsetof(fa_problem, in_dtype), offsetof(fa_problem, H_kv), '
+                   'sizeof(fa_tensor)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert got == [ctypes.sizeof(FaProblem), FaProblem.scale.offset, FaProblem.in_dtype.offset,
+                   FaProblem.H_kv.offset, ctypes.sizeof(FaTensor)]
 
 
 def test_workspace_sizes(lib):
     p = prob(2, 3, 130, 64)
+    # grouped-query attention does not change the workspace (all per query head)
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, Hkv=1))) == \
+        lib.fa_bob_workspace_bytes(ctypes.byref(p))
     # D, alpha, E ([B,H,N] fp32 each), then four chain inits per row padded to 128 rows
     assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == (3 * 2 * 3 * 130 + 4 * 2 * 3 * 256) * 4
     assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 2 * 3 * 130 * 4
@@ -86,6 +110,9 @@ def bob(lib, p, tensors=None, lse=FAKE, ws=FAKE, ws_bytes=1 << 30):
     (prob(scale=float("nan")), 5),
     (prob(scale=float("inf")), 5),
     (prob(N=(1 << 30) + 1), 2),
+    (prob(H=2, Hkv=3), 2),   # more key/value heads than query heads
+    (prob(H=4, Hkv=3), 2),   # not a divisor
+    (prob(H=2, Hkv=-1), 2),
 ])
 def test_problem_validation(lib, p, status):
     assert bob(lib, p) == status

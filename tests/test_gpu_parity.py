@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import make_inputs
-from oracle import bob_dense
+from oracle import bob_dense, bob_dense_gqa
 from tests.gpu_helpers import NAMES, host, rel, run_path, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -150,4 +150,61 @@ def test_causal_deterministic():
     a = run_path(t, causal=True)
     b = run_path(t, causal=True)
     for key in ("O", "L", "dQ", "dK", "dV", "gQ", "gK", "gV", "gdO", "alpha", "E"):
+        assert bool((a[key] == b[key]).all()), key
+
+
+# ---------------------------------------------------------------- grouped-query / multi-query attention
+
+KV_KEYS = ("dK", "dV", "gK", "gV")
+
+
+def check_case_gqa(B, H, Hkv, N, d, dtype, seed, causal=False, layout="bhnd", scale=None):
+    """K, V, U_K, U_V with Hkv heads shared by groups of H / Hkv query heads,
+    against the grouped-query oracle (key-side outputs summed over each group)."""
+    say(f"case GQA B={B} H={H} Hkv={Hkv} N={N} d={d} {dtype} seed={seed} causal={causal} layout={layout}")
+    raw, f64 = make_inputs(B, H, N, d, seed, dtype, H_kv=Hkv)
+    tau = scale if scale is not None else 1.0 / np.sqrt(d)
+    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal)
+    ref = {}
+    for b in range(B):
+        r = bob_dense_gqa(*(f64[n][b] for n in NAMES), tau, causal)
+        for key in ALL:
+            ref.setdefault(key, np.zeros((B,) + r[key].shape))[b] = r[key]
+    for key in KV_KEYS:
+        assert tuple(got[key].shape) == (B, Hkv, N, d), key
+    errs = {k: rel(host(got[k]), ref[k]) for k in ALL}
+    say("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, bad
+    return got
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,causal", [
+    (1, 4, 1, 100, 64, False),   # MQA, ragged single tile
+    (2, 6, 2, 130, 64, True),    # GQA, causal, ragged resident block
+    (1, 2, 1, 640, 64, False),   # ten streamed tiles per query head, crossing a head boundary
+    (1, 8, 2, 300, 128, False),  # d = 128
+    (1, 4, 2, 257, 128, True),
+    (1, 3, 3, 70, 64, False),    # H_kv = H (multi-head through the grouped path)
+])
+def test_gqa_bf16_shapes(B, H, Hkv, N, d, causal):
+    check_case_gqa(B, H, Hkv, N, d, "bf16", 800 + H + Hkv + N + d, causal=causal)
+
+
+def test_gqa_fp32():
+    check_case_gqa(1, 4, 1, 128, 64, "fp32", 820)
+    check_case_gqa(1, 2, 1, 90, 64, "fp32", 821, causal=True)
+
+
+def test_gqa_strided_and_scaled():
+    check_case_gqa(1, 4, 2, 150, 64, "bf16", 822, layout="bnhd")
+    check_case_gqa(1, 4, 1, 200, 64, "bf16", 823, scale=0.1, causal=True)
+
+
+def test_gqa_deterministic():
+    raw, _ = make_inputs(1, 4, 333, 64, 824, "bf16", H_kv=1)
+    t = to_device(raw, "bf16")
+    a = run_path(t)
+    b = run_path(t)
+    for key in ("dK", "dV", "gK", "gV", "gQ", "gdO"):
         assert bool((a[key] == b[key]).all()), key

@@ -111,6 +111,50 @@ def test_gpt2c_16k_causal_workload_sampled():
     _sampled("gpt2c_16k")
 
 
+def test_mqa_32k_workload_sampled():
+    """The pages' multi-query shape (8 query heads sharing one key/value head),
+    N = 32768, d = 64: key-side outputs on stored sampled columns (sums over
+    the 8 query heads, written by tests/golden/make_golden.py), row outputs of
+    two query heads on sampled rows computed by the oracle in-test against the
+    shared head, and the sum_j gK_j = sum_j gV_j = 0 property."""
+    w = WORKLOADS["mqa_32k"]
+    g = np.load(os.path.join(GOLDEN, "mqa_32k_cols.npz"), allow_pickle=False)
+    say("workload mqa_32k: GPU path")
+    raw, f64 = workload_inputs(w)
+    got = run_path(to_device(raw, w.dtype), causal=w.causal)
+    del raw
+    assert tuple(got["gK"].shape) == (w.B, w.Hkv, w.N, w.d)
+    for key in ("gK", "gV", "dK", "dV"):
+        vals = np.stack([host(got[key][b, h, c]) for (b, h), c in zip(g["heads"], g["cols"])])
+        e = rel(vals, g[key])
+        say(f"  {key} sampled columns {e:.2e}")
+        assert e <= TOL[w.dtype], key
+    for key in ("L", "D", "alpha", "E"):
+        vals = np.array([float(got[key][b, h, r]) for b, h, r in g["state_rows"]])
+        e = rel(vals, g[key])
+        say(f"  {key} stored rows {e:.2e}")
+        assert e <= TOL[w.dtype], key
+    G = w.H // w.Hkv
+    rng = np.random.default_rng(5000 + w.seed)
+    for h in (0, w.H - 1):
+        hk = h // G
+        rows = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, size=22, replace=False)]))
+        say(f"  oracle rows query head {h} (key/value head {hk})")
+        r = row_pass(f64["q"][0, h], f64["k"][0, hk], f64["v"][0, hk], f64["do"][0, h], f64["uq"][0, h],
+                     f64["uk"][0, hk], f64["uv"][0, hk], w.scale, rows=rows, outputs="all", strip=4,
+                     threads=oracle_threads(), causal=w.causal)
+        for key in ("gQ", "gdO", "dQ", "O", "L", "D", "alpha", "E"):
+            e = rel(host(got[key][0, h][rows]), r[key])
+            say(f"  {key} query head {h} sampled rows {e:.2e}")
+            assert e <= TOL[w.dtype], (key, h)
+    for key in ("gK", "gV"):
+        x = got[key].double()
+        s_ = x.sum(dim=2).abs().amax().item()
+        bound = 2e-2 * np.sqrt(w.N * G) * x.abs().amax().item()
+        say(f"  |sum_j {key}_j| = {s_:.3e} (bound {bound:.3e})")
+        assert s_ <= bound, key
+
+
 def test_max_workload_sampled_and_memory():
     import torch
 
