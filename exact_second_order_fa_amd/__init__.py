@@ -18,6 +18,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_OK = 0
+# fa_version() the binding needs: 1.1 added fa_problem.H_kv; an older library
+# would read key-side tensors with the query-head count.
+MIN_VERSION = 10100
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_STRIDE", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_UNSUPPORTED", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP",
@@ -53,8 +56,9 @@ class FaTensor(ctypes.Structure):
 _LIB = None
 
 
-def load_library(path: str | None = None) -> ctypes.CDLL:
-    """Load libfa.so (once) and declare the C signatures."""
+def load_library(path: str | None = None, check_version: bool = True) -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures.  A library older than
+    this binding (fa_version() < MIN_VERSION, same major version) is refused."""
     global _LIB
     if _LIB is not None and path is None:
         return _LIB
@@ -80,6 +84,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.fa_bob.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, vp]
     lib.fa_bob_phase.restype = ctypes.c_int
     lib.fa_bob_phase.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, ctypes.c_int32, vp]
+    ver = lib.fa_version()
+    if check_version and not (MIN_VERSION <= ver < (MIN_VERSION // 10000 + 1) * 10000):
+        raise FaLibraryError(f"{p} has version {ver}; this binding needs {MIN_VERSION} up to the next major "
+                             "version (rebuild with `python -m exact_second_order_fa_amd.build`)")
     if path is None:
         _LIB = lib
     return lib

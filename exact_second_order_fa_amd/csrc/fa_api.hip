@@ -14,7 +14,7 @@ using fa::Args;
 using fa::bf16;
 using fa::TDesc;
 
-constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;  // 1.1: fa_problem.H_kv
 
 struct Ctx {
   int64_t B, H, N, d;

@@ -527,12 +527,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int t = t0; t < t1; ++t) {
         dma_wait();
         __syncthreads();
-        const char* next = lds + ((u + 1) & 1) * STAGE;
-        if (t + 1 < nt) {
-          copy_tile(g, t + 1, next);
-        } else if (g + 1 < a.G) {
-          copy_tile(g + 1, t_begin, next);
-        }
+        // The next tile: t + 1 of this head, else the next head's first.
+        const bool wrap = t + 1 >= nt;
+        const int gn = wrap ? g + 1 : g, tn = wrap ? t_begin : t + 1;
+        if (gn < a.G) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
         tile_body(t, u & 1, mode_c);
         ++u;
       }

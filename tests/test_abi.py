@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 10000
+    assert lib.fa_version() == 10100  # 1.1.0: fa_problem gained H_kv
     for code in range(8):
         s = lib.fa_status_str(code).decode()
         assert s and s != "unknown status"
@@ -157,3 +157,22 @@ def test_fwd_validation(lib):
     p = prob()
     assert lib.fa_fwd(ctypes.byref(p), t(), t(), t(ptr=0), t(), FAKE, None) == 1
     assert lib.fa_fwd(ctypes.byref(p), t(), t(), t(), t(), 0, None) == 1
+
+
+def test_binding_refuses_an_older_library(tmp_path):
+    """A library from before fa_problem.H_kv would index key-side tensors with
+    the query-head count; the binding refuses to load one (stub built with gcc,
+    exporting the ABI's names; never called beyond fa_version)."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = [n for n in fa.SYMBOLS if n != "fa_version"]
+    src = tmp_path / "old.c"
+    src.write_text("int fa_version(void) { return 10000; }\n" + "".join(f"int {n}(void) {{ return 0; }}\n" for n in names))
+    so = tmp_path / "libold.so"
+    subprocess.run([cc, "-shared", "-fPIC", "-o", str(so), str(src)], check=True)
+    with pytest.raises(fa.FaLibraryError):
+        fa.load_library(str(so))
