@@ -40,6 +40,14 @@ PAGES_MS = {
     "gpt2c_16k": {"ms": 365.73, "gpu": "A100 80GB", "source": "FlashBoB Table 1, d=64"},
     "c128_16k": {"ms": 263.6, "gpu": "B300", "source": "FlashBoB Table 1, d=128"},
 }
+# The pages' schedule ablation (three-pass vs two-pass; GPT-2 Small shape,
+# batch 4, on A100), context only.
+PAGES_ABLATION = {
+    "gpt2c_4k": {"three_pass_ms": 27.30, "two_pass_ms": 25.80, "ratio": 1.06, "gpu": "A100 80GB",
+                 "source": "FlashBoB Table 8"},
+    "gpt2c_16k": {"three_pass_ms": 389.14, "two_pass_ms": 365.73, "ratio": 1.06, "gpu": "A100 80GB",
+                  "source": "FlashBoB Table 8"},
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bob_pass1_traffic.json")
 KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_bob.hip", "exact_second_order_fa_amd/csrc/fa_bob_ws.hip",
                   "exact_second_order_fa_amd/csrc/fa_lds.h",
@@ -88,10 +96,11 @@ class Runner:
                               device="cuda")
         torch.cuda.synchronize()
 
-    def bob(self, phase=None):
+    def bob(self, phase=None, schedule=None):
         t, g = self.t, self.outs
         self.fa.fa_bob(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], t["uq"], t["uk"], t["uv"],
-                       gq=g[0], gk=g[1], gv=g[2], gdo=g[3], ws=self.ws, phase=phase, causal=self.w.causal)
+                       gq=g[0], gk=g[1], gv=g[2], gdo=g[3], ws=self.ws, phase=phase, causal=self.w.causal,
+                       schedule=schedule)
 
     def fwd(self):
         self.fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], o=self.o, lse=self.lse, causal=self.w.causal)
@@ -170,6 +179,52 @@ def cpu_baseline(w, heads):
                       f"column passes in float64, {dt:.1f} s"}
 
 
+def streamed_bytes(w, schedule):
+    """Algorithmic bytes the sweeps stream from the other side (bf16 tiles and
+    fp32 chain inits), with the row and column blocks of 128: the two-pass row
+    pass streams K, V, U_K, U_V (8 d bytes per key per row block), the column
+    pass Q, dO, U_Q and four row scalars (6 d + 16 bytes per row per key
+    block), the three-pass alpha sweep K and U_K (4 d bytes per key per row
+    block).  Causal attention streams half."""
+    blocks = (w.N + 127) // 128
+    row = blocks * w.N * 8 * w.d
+    col = blocks * w.N * (6 * w.d + 16)
+    alpha = blocks * w.N * 4 * w.d if schedule == 2 else 0
+    f = w.B * w.H * (0.5 if w.causal else 1.0)
+    return {"row_pass": row * f, "column_pass": col * f, "alpha_sweep": alpha * f, "total": (row + col + alpha) * f}
+
+
+def ablation(names, reps=5):
+    """Three-pass vs two-pass ([FlashBoB] appendix G.1) on the same kernel
+    machinery: the two-pass row pass with one wave per SIMD (the kernel the
+    three-pass row sweep is built from) against the three-pass schedule, and
+    the production two-pass (warp-specialised row pass) beside them."""
+    import torch
+
+    from fa_inputs import WORKLOADS
+
+    out = {}
+    for name in names:
+        w = WORKLOADS[name]
+        r = Runner(w)
+        res = {}
+        for label, sched, nph in (("two_pass", 0, 3), ("two_pass_1wave", 1, 3), ("three_pass", 2, 4)):
+            ms = time_plain(lambda: r.bob(schedule=sched), reps)
+            phases = [time_plain(lambda ph=ph: r.bob(phase=ph, schedule=sched), reps) for ph in range(nph)]
+            res[label] = {"ms": round(ms, 3), "phase_ms": [round(x, 3) for x in phases]}
+        sb2, sb3 = streamed_bytes(w, 0), streamed_bytes(w, 2)
+        res["ratio_three_over_two_1wave"] = round(res["three_pass"]["ms"] / res["two_pass_1wave"]["ms"], 3)
+        res["ratio_three_over_two"] = round(res["three_pass"]["ms"] / res["two_pass"]["ms"], 3)
+        res["streamed_bytes"] = {"two_pass": sb2["total"], "three_pass": sb3["total"],
+                                 "saving_of_three_pass": round(1 - sb2["total"] / sb3["total"], 4)}
+        if name in PAGES_ABLATION:
+            res["pages_context"] = PAGES_ABLATION[name]
+        out[name] = res
+        del r
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +233,9 @@ def main():
     ap.add_argument("--workload", default="mid")
     ap.add_argument("--sweep", default="hd128,long,max,gpt2c_4k,gpt2c_16k,c128_16k,mqa_32k",
                     help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--ablation", default="gpt2c_4k,gpt2c_16k",
+                    help="workloads of the three-pass vs two-pass schedule ablation ('' for none)")
+    ap.add_argument("--only-ablation", action="store_true", help="run only the schedule ablation (profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -203,6 +261,11 @@ def main():
         return
 
     from fa_inputs import WORKLOADS
+
+    abl_names = [s_ for s_ in args.ablation.split(",") if s_]
+    if args.only_ablation:
+        print(json.dumps({"ablation": ablation(abl_names)}), flush=True)
+        return
 
     w = WORKLOADS[args.workload]
     r = Runner(w)
@@ -257,6 +320,10 @@ def main():
                        "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)},
         "sweep": sweep,
     }
+    if abl_names:
+        del r
+        torch.cuda.empty_cache()
+        line["schedule_ablation"] = ablation(abl_names)
     if not args.no_cpu:
         nh = w.B * w.H if args.cpu_heads <= 0 else min(args.cpu_heads, w.B * w.H)
         line["cpu_baseline"] = cpu_baseline(w, nh)

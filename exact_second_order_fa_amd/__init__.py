@@ -29,7 +29,9 @@ FA_BF16, FA_FP32 = 0, 1
 
 # Exported symbols (kept equal to the declarations in include/fa.h).
 SYMBOLS = ("fa_version", "fa_status_str", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_bob_workspace_bytes", "fa_bob", "fa_bob_phase")
+           "fa_bob_workspace_bytes", "fa_bob", "fa_bob_phase", "fa_bob_schedule")
+# Schedules of fa_bob_schedule (include/fa.h).
+SCHED_TWO_PASS, SCHED_TWO_PASS_1WAVE, SCHED_THREE_PASS = 0, 1, 2
 
 
 class FaLibraryError(RuntimeError):
@@ -84,6 +86,9 @@ def load_library(path: str | None = None, check_version: bool = True) -> ctypes.
     lib.fa_bob.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, vp]
     lib.fa_bob_phase.restype = ctypes.c_int
     lib.fa_bob_phase.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, ctypes.c_int32, vp]
+    lib.fa_bob_schedule.restype = ctypes.c_int
+    lib.fa_bob_schedule.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, ctypes.c_int32,
+                                    ctypes.c_int32, vp]
     ver = lib.fa_version()
     if check_version and not (MIN_VERSION <= ver < (MIN_VERSION // 10000 + 1) * 10000):
         raise FaLibraryError(f"{p} has version {ver}; this binding needs {MIN_VERSION} up to the next major "
@@ -226,12 +231,14 @@ def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None
 
 
 def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=None, gdo=None,
-           ws=None, stream=None, phase=None, causal=False):
+           ws=None, stream=None, phase=None, causal=False, schedule=None):
     """Backward-over-backward: gradients of <dQ,U_Q> + <dK,U_K> + <dV,U_V> with
     respect to Q, K, V and dO (k, v, uk, uv and gK, gV may have fewer heads
     than q: grouped-query / multi-query attention).  Returns (gQ, gK, gV, gdO, ws) with
     ws = [D | alpha | E], each [B, H, N] fp32.  ``phase`` (0, 1 or 2) calls
-    fa_bob_phase instead, launching only that kernel."""
+    fa_bob_phase instead, launching only that kernel.  ``schedule`` (one of
+    the SCHED_* constants) calls fa_bob_schedule: the schedule ablation of
+    the pages' appendix G.1 (phases 0-3 for the three-pass schedule)."""
     B, H, N, d, Hkv = _check_inputs((q, dout, uq), (k, v, uk, uv))
     p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
     gq, gdo = _f32_like(q, gq), _f32_like(q, gdo)
@@ -243,7 +250,11 @@ def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=N
             ctypes.c_void_p(lse.data_ptr()), tensor_arg(dout), tensor_arg(uq), tensor_arg(uk),
             tensor_arg(uv), tensor_arg(gq), tensor_arg(gk), tensor_arg(gv), tensor_arg(gdo),
             ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel() * ws.element_size())]
-    if phase is None:
+    if schedule is not None:
+        _call("fa_bob_schedule", lib.fa_bob_schedule(*args, ctypes.c_int32(schedule),
+                                                      ctypes.c_int32(-1 if phase is None else phase),
+                                                      _stream(stream)))
+    elif phase is None:
         _call("fa_bob", lib.fa_bob(*args, _stream(stream)))
     else:
         _call("fa_bob_phase", lib.fa_bob_phase(*args, ctypes.c_int32(phase), _stream(stream)))

@@ -157,28 +157,52 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
                      st, a);
 }
 
-// phase < 0: the whole BoB (row scalars, row pass, column pass); 0, 1, 2:
-// only that kernel.
+// Schedules of the BoB ([FlashBoB] section 4.3 and appendix G.1):
+//   0: two-pass (row-scalar kernel, row pass, column pass), the production path;
+//   1: two-pass with the single-wave row pass at bf16, d = 64 (the same kernels
+//      as 0 elsewhere), the baseline of the schedule ablation;
+//   2: three-pass (row scalars, alpha sweep, row pass with known alpha, column
+//      pass), bf16 only.
+// phase < 0 runs the whole schedule; otherwise only that kernel.
 template <typename T, int D, bool RHO1, bool C>
-void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int phase) {
-  const dim3 g(grid_rows(c)), b(fa::kThreads);
-  if (phase < 0 || phase == 0) launch_rowscalar<T, D>(c, a, st);
-  if (phase < 0 || phase == 1) {
-    if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass1_ws_kernel<RHO1, C>), g, dim3(2 * fa::kThreads), 0, st, a);
-    else if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C>), g, b, 0, st, a);
-    else
-      hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
-  }
-  if (phase < 0 || phase == 2) {
-    const dim3 gc(grid_cols(c));
-    if constexpr (sizeof(T) == 2 && D == 64)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), gc, b, 0, st, a);
-    else if constexpr (sizeof(T) == 2 && D == 128)
-      hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), gc, b, 0, st, a);
-    else
-      hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), gc, b, 0, st, a);
+void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int phase) {
+  const dim3 g(grid_rows(c)), b(fa::kThreads), gc(grid_cols(c));
+  auto want = [&](int ph) { return phase < 0 || phase == ph; };
+  if (want(0)) launch_rowscalar<T, D>(c, a, st);
+  const int col_phase = schedule == 2 ? 3 : 2;
+  if constexpr (sizeof(T) == 2) {
+    if (schedule == 2) {
+      if (want(1)) {
+        if constexpr (D == 64)
+          hipLaunchKernelGGL((fa::bob_alpha_dma_kernel<D, 128, RHO1, C>), g, b, 0, st, a);
+        else
+          hipLaunchKernelGGL((fa::bob_alpha_dma_kernel<D, 64, RHO1, C>), g, b, 0, st, a);
+      }
+      if (want(2)) {
+        if constexpr (D == 64)
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C, 1>), g, b, 0, st, a);
+        else
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C, 1>), g, b, 0, st, a);
+      }
+    } else if (want(1)) {
+      if constexpr (D == 64) {
+        if (schedule == 0)
+          hipLaunchKernelGGL((fa::bob_pass1_ws_kernel<RHO1, C>), g, dim3(2 * fa::kThreads), 0, st, a);
+        else
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C>), g, b, 0, st, a);
+      } else {
+        hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C>), g, b, 0, st, a);
+      }
+    }
+    if (want(col_phase)) {
+      if constexpr (D == 64)
+        hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), gc, b, 0, st, a);
+      else
+        hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), gc, b, 0, st, a);
+    }
+  } else {
+    if (want(1)) hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
+    if (want(2)) hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), gc, b, 0, st, a);
   }
 }
 
@@ -209,9 +233,9 @@ struct BwdL {
 };
 template <typename T, int D, bool C>
 struct BobL {
-  static void run(const Ctx& c, const Args& a, hipStream_t st, int phase) {
-    if (c.rho == 1.0f) launch_bob<T, D, true, C>(c, a, st, phase);
-    else launch_bob<T, D, false, C>(c, a, st, phase);
+  static void run(const Ctx& c, const Args& a, hipStream_t st, int schedule, int phase) {
+    if (c.rho == 1.0f) launch_bob<T, D, true, C>(c, a, st, schedule, phase);
+    else launch_bob<T, D, false, C>(c, a, st, schedule, phase);
   }
 };
 
@@ -305,9 +329,12 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
 static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o,
                           const float* lse, fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq,
                           fa_tensor gk, fa_tensor gv, fa_tensor gdo, void* workspace, size_t workspace_bytes,
-                          int phase, void* stream) {
+                          int schedule, int phase, void* stream) {
   Ctx c;
   FA_CHECK(check_problem(p, &c));
+  if (schedule < 0 || schedule > 2) return FA_ERR_UNSUPPORTED;
+  if (schedule == 2 && !c.bf) return FA_ERR_UNSUPPORTED;
+  if (phase < -1 || phase > (schedule == 2 ? 3 : 2)) return FA_ERR_UNSUPPORTED;
   FA_CHECK(check_tensor(c, q, c.esize));
   FA_CHECK(check_tensor(c, k, c.esize));
   FA_CHECK(check_tensor(c, v, c.esize));
@@ -344,14 +371,14 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   a.ps = a.D + 3 * nrow;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  dispatch3<BobL>(c, a, st, phase);
+  dispatch3<BobL>(c, a, st, schedule, phase);
   return launched();
 }
 
 fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const float* lse,
                  fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq, fa_tensor gk, fa_tensor gv,
                  fa_tensor gdo, void* workspace, size_t workspace_bytes, void* stream) {
-  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, -1, stream);
+  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, 0, -1, stream);
 }
 
 fa_status fa_bob_phase(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const float* lse,
@@ -359,7 +386,15 @@ fa_status fa_bob_phase(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor 
                        fa_tensor gv, fa_tensor gdo, void* workspace, size_t workspace_bytes, int32_t phase,
                        void* stream) {
   if (phase < 0 || phase > 2) return FA_ERR_UNSUPPORTED;
-  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, phase, stream);
+  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, 0, phase, stream);
+}
+
+fa_status fa_bob_schedule(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o,
+                          const float* lse, fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq,
+                          fa_tensor gk, fa_tensor gv, fa_tensor gdo, void* workspace, size_t workspace_bytes,
+                          int32_t schedule, int32_t phase, void* stream) {
+  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, schedule,
+                  phase, stream);
 }
 
 }  // extern "C"

@@ -92,7 +92,14 @@ __device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
 // Schedule of one tile (NSUB sub-tiles): scores(0); then for each sub-tile s
 // the elementwise work of s interleaved with the accumulations of s - 1, and
 // the scores of s + 1.
-template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL>
+//
+// SCHED = 1 is the second sweep of the three-pass schedule ([FlashBoB]
+// appendix G.1): alpha is known (written by bob_alpha_dma_kernel), so
+//   d~P = C + F dPD - alpha dP,  h = F - alpha,  E = sum_j P d~P directly,
+//   G  += P U_V + (P h) V        (= gdo, no correction),
+//   Om += (P d~P) K + dS U_K,    Bk += P K,      gq = tau (Om - E Bk)
+// (the delayed E-correction), with one accumulation fewer than SCHED = 0.
+template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL, int SCHED = 0>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_dma_kernel(Args a) {
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
@@ -131,6 +138,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float Li = row < N ? a.lse[rv + row] : 0.0f;
   const float Di = row < N ? a.D[rv + row] : 0.0f;
   const float nl2 = -Li * kLog2e;
+  const float Ai = (SCHED == 1 && row < N) ? a.alpha[rv + row] : 0.0f;  // known alpha (three-pass)
 
   Reader<D, TS> rd;
   rd.init();
@@ -202,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       mfma_acc(ag[db], xv, cpf.f[s2]);
       mfma_acc(aom[db], xk, cpt.f[s2]);
       mfma_acc(aom[db], xuk, cds.f[s2]);
-      mfma_acc(ar[db], xk, cds.f[s2]);
+      if constexpr (SCHED == 0) mfma_acc(ar[db], xk, cds.f[s2]);
       mfma_acc(abk[db], xk, cp.f[s2]);
     };
     // Elementwise work on elements 4*part .. 4*part+3 of the current sub-tile.
@@ -215,15 +223,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float F = RHO1 ? f[idx] : f[idx] * a.rho;
         const float dpd = dp[idx] - Di;
         const float t0 = fmaf(F, dpd, c[idx]);
-        const float pf = p * F, pt = p * t0;
-        alpha_p += pf;
-        eo_p += pt;
-        const bf16 ptb = (bf16)pt;
-        eob_p += (float)ptb;
-        cp.f[idx >> 3][idx & 7] = (bf16)p;
-        cpf.f[idx >> 3][idx & 7] = (bf16)pf;
-        cpt.f[idx >> 3][idx & 7] = ptb;
-        cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
+        if constexpr (SCHED == 0) {
+          const float pf = p * F, pt = p * t0;
+          alpha_p += pf;
+          eo_p += pt;
+          const bf16 ptb = (bf16)pt;
+          eob_p += (float)ptb;
+          cp.f[idx >> 3][idx & 7] = (bf16)p;
+          cpf.f[idx >> 3][idx & 7] = (bf16)pf;
+          cpt.f[idx >> 3][idx & 7] = ptb;
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
+        } else {
+          // cpf carries P h, cpt carries P d~P; E is summed directly.
+          const float pt = p * fmaf(-Ai, dp[idx], t0);
+          eo_p += pt;
+          const bf16 ptb = (bf16)pt;
+          eob_p += (float)ptb;
+          cp.f[idx >> 3][idx & 7] = (bf16)p;
+          cpf.f[idx >> 3][idx & 7] = (bf16)(p * (F - Ai));
+          cpt.f[idx >> 3][idx & 7] = ptb;
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
+        }
       }
     };
 
@@ -295,12 +315,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 
   acc_fence<NDB>(ag, aom, ar, abk);
-  const float alpha = half_sum(alpha_p);
-  const float eo = half_sum(eo_p);
+  // SCHED 0: alpha and E° from the sweep; SCHED 1: alpha known, E summed.
+  const float alpha = SCHED == 0 ? half_sum(alpha_p) : Ai;
+  const float esum = half_sum(eo_p);
+  const float eo = SCHED == 0 ? esum : esum + Ai * Di;  // E° = E + alpha D
   const float eob = half_sum(eob_p);
   if (row < N && hh == 0) {
-    a.alpha[rv + row] = alpha;
-    a.E[rv + row] = eo - alpha * Di;
+    if constexpr (SCHED == 0) a.alpha[rv + row] = alpha;
+    a.E[rv + row] = SCHED == 0 ? eo - alpha * Di : esum;
   }
   if (hh == 0) {
     // Chain inits of the column pass for this row (see bob_pass2_dma_kernel):
@@ -319,22 +341,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   float* gdo = head_out(a.r3, wk.b, wk.h);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    float ov[16];
-    if (row < N) {
-      const float* orow = o.p + (int64_t)row * o.sn + db * 32 + 4 * hh;
+    if constexpr (SCHED == 0) {
+      float ov[16];
+      if (row < N) {
+        const float* orow = o.p + (int64_t)row * o.sn + db * 32 + 4 * hh;
 #pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(orow + 8 * b4);
+        for (int b4 = 0; b4 < 4; ++b4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(orow + 8 * b4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[4 * b4 + e] = x[e];
+          for (int e = 0; e < 4; ++e) ov[4 * b4 + e] = x[e];
+        }
       }
+      store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx] - alpha * ov[idx]; });
+      store_out(gq, a.r0.sn, row, N, db,
+                [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eob * abk[db][idx]); });
+    } else {
+      store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx]; });
+      store_out(gq, a.r0.sn, row, N, db, [&](int idx) { return a.tau * (aom[db][idx] - eob * abk[db][idx]); });
     }
-    store_out(gdo, a.r3.sn, row, N, db, [&](int idx) { return ag[db][idx] - alpha * ov[idx]; });
-    store_out(gq, a.r0.sn, row, N, db,
-              [&](int idx) { return a.tau * (aom[db][idx] - alpha * ar[db][idx] - eob * abk[db][idx]); });
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// alpha sweep: the first pass of the three-pass schedule ([FlashBoB]
+// appendix G.1), kept for the schedule ablation.  Streams only K and U_K
+// (the operands of F):  alpha_i = sum_j P_ij F_ij  with
+//   S^T = K Q^T,  F^T = K U_Q^T + U_K Q^T,  P = exp(tau S - L).
+// The score chains of sub-tile s + 1 are issued before the elementwise work
+// of sub-tile s, so the matrix cores and the VALU overlap.
+template <int D, int TS, bool RHO1, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_alpha_dma_kernel(Args a) {
+  typedef SwTile<D, TS> W;
+  constexpr int NKS = D / 16, NSUB = TS / 32;
+  constexpr int STAGE = 2 * W::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float kbias[TS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<bf16> q = head_of<bf16>(a.q, wk.b, wk.h), uq = head_of<bf16>(a.uq, wk.b, wk.h);
+  HeadPtr<bf16> src[2] = {head_of<bf16>(a.k, wk.b, wk.hk), head_of<bf16>(a.uk, wk.b, wk.hk)};
+  const int nt = (N + TS - 1) / TS;
+  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
+  const int t_diag = CAUSAL ? wk.rb * kResRows / TS : nt;
+  const bool ragged = !CAUSAL && (N % TS) != 0;
+
+  Dma<D, TS, 2> dma;
+  dma.init(src);
+  dma.copy(0, N, lds);
+  fill_bias<TS>(kbias, (nt - 1) * TS, N);
+
+  bf16x8 qf[NKS], uqf[NKS];
+  load_resident<bf16, D>(qf, q.p, q.sn, row, N, a.pow2);
+  load_resident<bf16, D>(uqf, uq.p, uq.sn, row, N, a.pow2);
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float Li = row < N ? a.lse[rv + row] : 0.0f;
+  const float nl2 = -Li * kLog2e;
+
+  Reader<D, TS> rd;
+  rd.init();
+  float alpha_p = 0.0f;
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load of the compiler's own in the loop
+
+  auto tile_body = [&](int t, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    const char* tk = lds + (t & 1) * STAGE;
+    const char* tuk = tk + W::BYTES;
+    auto scores = [&](int sub, f32x16& s, f32x16& f) {
+      if constexpr (MODE == 1) {
+        s = row_init<TS>(kbias, sub);
+      } else if constexpr (MODE == 2) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx)
+          s[idx] = (t * TS + sub * 32 + acc_pos(idx, hh) <= row) ? 0.0f : -INFINITY;
+        asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 xk = rd_row<D, TS>(tk, rd, sub, ks);
+        const bf16x8 xuk = rd_row<D, TS>(tuk, rd, sub, ks);
+        if (MODE == 0 && ks == 0) {
+          s = mfma_first(xk, qf[0]);
+        } else {
+          mfma_v(s, xk, qf[ks]);
+        }
+        if (ks == 0) {
+          f = mfma_first(xk, uqf[0]);
+        } else {
+          mfma_v(f, xk, uqf[ks]);
+        }
+        mfma_v(f, xuk, qf[ks]);
+      }
+    };
+    f32x16 s[2], f[2];
+    scores(0, s[0], f[0]);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      f32x16& sc = s[sub & 1];
+      f32x16& fc = f[sub & 1];
+      asm volatile("s_nop 7\n\ts_nop 4" : "+v"(sc), "+v"(fc));  // MFMA result -> VALU read
+      if (sub + 1 < NSUB) scores(sub + 1, s[(sub + 1) & 1], f[(sub + 1) & 1]);
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[idx], a.c1, nl2));
+        alpha_p = fmaf(p, RHO1 ? fc[idx] : fc[idx] * a.rho, alpha_p);
+      }
+    }
+  };
+  auto run = [&](int t0, int t1, auto mode_c) {
+    for (int t = t0; t < t1; ++t) {
+      dma_wait();
+      __syncthreads();
+      if (t + 1 < t_end) dma.copy((t + 1) * TS, N, lds + ((t + 1) & 1) * STAGE);
+      tile_body(t, mode_c);
+    }
+  };
+  if constexpr (CAUSAL) {
+    run(0, t_diag, std::integral_constant<int, 0>{});
+    run(t_diag, t_end, std::integral_constant<int, 2>{});
+  } else {
+    run(0, ragged ? nt - 1 : nt, std::integral_constant<int, 0>{});
+    if (ragged) run(nt - 1, nt, std::integral_constant<int, 1>{});
+  }
+  const float alpha = half_sum(alpha_p);
+  if (row < N && hh == 0) a.alpha[rv + row] = alpha;
+}
 
 // ---------------------------------------------------------------------------
 // Pass 2 (column-major).  Resident per wave: 32 key rows j with k_j, u_K,j

@@ -174,6 +174,36 @@ fa_status fa_bob_phase(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor 
                        void* workspace, size_t workspace_bytes, int32_t phase,
                        void* stream);
 
+/* Schedules of fa_bob_schedule. */
+typedef enum fa_schedule {
+  FA_SCHED_TWO_PASS = 0,       /* what fa_bob runs */
+  FA_SCHED_TWO_PASS_1WAVE = 1, /* two-pass with the single-wave row pass (bf16, d = 64; else = 0) */
+  FA_SCHED_THREE_PASS = 2      /* three-pass schedule of [FlashBoB] appendix G.1 (bf16 only) */
+} fa_schedule;
+
+/*
+ * fa_bob_schedule -- fa_bob under a chosen schedule, for the schedule
+ * ablation of [FlashBoB] appendix G.1 ("Three-pass versus two-pass").  Every
+ * schedule computes the same outputs and workspace values (D, alpha, E) up to
+ * rounding; they differ in how many sweeps stream the key side:
+ *   FA_SCHED_TWO_PASS, FA_SCHED_TWO_PASS_1WAVE: phases 0 (row scalars D), 1
+ *     (row pass: gq, gdo, alpha, E with the affine corrections of section 4.2),
+ *     2 (column pass: gk, gv);
+ *   FA_SCHED_THREE_PASS: phases 0 (D), 1 (alpha-only row sweep, streams K and
+ *     U_K), 2 (row pass with alpha known: gq by the delayed E-correction, gdo,
+ *     E), 3 (column pass).
+ * phase = -1 runs the whole schedule; calling its phases in order on one
+ * stream is the same.  Arguments otherwise as fa_bob.  Errors: an unknown
+ * schedule, a phase outside the schedule, or FA_SCHED_THREE_PASS with fp32
+ * inputs return FA_ERR_UNSUPPORTED before anything is launched.
+ */
+fa_status fa_bob_schedule(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
+                          fa_tensor o, const float* lse, fa_tensor dout,
+                          fa_tensor uq, fa_tensor uk, fa_tensor uv,
+                          fa_tensor gq, fa_tensor gk, fa_tensor gv, fa_tensor gdo,
+                          void* workspace, size_t workspace_bytes, int32_t schedule,
+                          int32_t phase, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

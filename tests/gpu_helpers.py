@@ -39,7 +39,7 @@ def to_device(raw, dtype, layout="bhnd"):
     return out
 
 
-def run_path(t, scale=None, with_bwd=True, layout="bhnd", causal=False):
+def run_path(t, scale=None, with_bwd=True, layout="bhnd", causal=False, schedule=None):
     """fa_fwd, fa_bwd (optional) and fa_bob on device tensors; returns torch
     tensors on the GPU."""
     import torch
@@ -62,7 +62,7 @@ def run_path(t, scale=None, with_bwd=True, layout="bhnd", causal=False):
     outs = [empty_like_out(t[n]) for n in ("q", "k", "k", "q")]  # gQ, gK, gV, gdO
     gq, gk, gv, gdo, ws = fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"],
                                     scale=scale, gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3],
-                                    causal=causal)
+                                    causal=causal, schedule=schedule)
     B, H, N, _ = t["q"].shape
     D, alpha, E = fa.split_workspace(ws, B, H, N)
     res.update(gQ=gq, gK=gk, gV=gv, gdO=gdo, D=D, alpha=alpha, E=E)

@@ -176,3 +176,27 @@ def test_binding_refuses_an_older_library(tmp_path):
     subprocess.run([cc, "-shared", "-fPIC", "-o", str(so), str(src)], check=True)
     with pytest.raises(fa.FaLibraryError):
         fa.load_library(str(so))
+
+
+def sched(lib, p, schedule, phase, ts=None):
+    ts = ts or [t() for _ in range(12)]
+    return lib.fa_bob_schedule(ctypes.byref(p), ts[0], ts[1], ts[2], ts[3], FAKE, ts[4], ts[5], ts[6], ts[7],
+                               ts[8], ts[9], ts[10], ts[11], FAKE, 1 << 30, schedule, phase, None)
+
+
+@pytest.mark.parametrize("schedule,phase,dt", [
+    (3, -1, fa.FA_BF16),      # unknown schedule
+    (-1, -1, fa.FA_BF16),
+    (2, -1, fa.FA_FP32),      # three-pass is bf16-only
+    (2, 4, fa.FA_BF16),       # phase outside the three-pass schedule
+    (0, 3, fa.FA_BF16),       # phase outside the two-pass schedule
+    (1, -2, fa.FA_BF16),
+])
+def test_schedule_validation(lib, schedule, phase, dt):
+    assert sched(lib, prob(dt=dt), schedule, phase) == 5
+
+
+def test_schedule_checks_tensors_too(lib):
+    bad = [t() for _ in range(12)]
+    bad[0] = t(ptr=0)
+    assert sched(lib, prob(), 2, -1, bad) == 1

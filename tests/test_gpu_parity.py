@@ -33,11 +33,12 @@ def oracle_heads(f64, scale, causal=False):
     return out
 
 
-def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd", causal=False):
-    say(f"case B={B} H={H} N={N} d={d} {dtype} seed={seed} scale={scale} layout={layout} causal={causal}")
+def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd", causal=False, schedule=None):
+    say(f"case B={B} H={H} N={N} d={d} {dtype} seed={seed} scale={scale} layout={layout} causal={causal} "
+        f"schedule={schedule}")
     raw, f64 = make_inputs(B, H, N, d, seed, dtype, cot_std=cot, qk_gain=qk)
     tau = scale if scale is not None else 1.0 / np.sqrt(d)
-    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal)
+    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal, schedule=schedule)
     ref = oracle_heads(f64, tau, causal)
     errs = {k: rel(host(got[k]), ref[k]) for k in ALL}
     say("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
@@ -158,13 +159,13 @@ def test_causal_deterministic():
 KV_KEYS = ("dK", "dV", "gK", "gV")
 
 
-def check_case_gqa(B, H, Hkv, N, d, dtype, seed, causal=False, layout="bhnd", scale=None):
+def check_case_gqa(B, H, Hkv, N, d, dtype, seed, causal=False, layout="bhnd", scale=None, schedule=None):
     """K, V, U_K, U_V with Hkv heads shared by groups of H / Hkv query heads,
     against the grouped-query oracle (key-side outputs summed over each group)."""
     say(f"case GQA B={B} H={H} Hkv={Hkv} N={N} d={d} {dtype} seed={seed} causal={causal} layout={layout}")
     raw, f64 = make_inputs(B, H, N, d, seed, dtype, H_kv=Hkv)
     tau = scale if scale is not None else 1.0 / np.sqrt(d)
-    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal)
+    got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal, schedule=schedule)
     ref = {}
     for b in range(B):
         r = bob_dense_gqa(*(f64[n][b] for n in NAMES), tau, causal)
@@ -208,3 +209,56 @@ def test_gqa_deterministic():
     b = run_path(t)
     for key in ("dK", "dV", "gK", "gV", "gQ", "gdO"):
         assert bool((a[key] == b[key]).all()), key
+
+
+
+# ---------------------------------------------------------------- schedule ablation ([FlashBoB] appendix G.1)
+
+THREE, ONE_WAVE = 2, 1
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 2, 100, 64, False),   # ragged single tile
+    (2, 3, 130, 64, True),
+    (1, 1, 640, 64, False),
+    (1, 2, 300, 128, False),
+    (1, 1, 513, 128, True),
+])
+def test_three_pass_schedule(B, H, N, d, causal):
+    check_case(B, H, N, d, "bf16", 1200 + N + d, causal=causal, schedule=THREE)
+
+
+def test_three_pass_schedule_strided_scaled_peaked():
+    check_case(1, 2, 150, 64, "bf16", 1210, layout="bnhd", schedule=THREE)
+    check_case(1, 2, 200, 64, "bf16", 1211, scale=0.1, schedule=THREE)
+    check_case(1, 2, 512, 64, "bf16", 1212, qk=2.0, cot=0.1, schedule=THREE)
+
+
+def test_three_pass_schedule_grouped_query():
+    check_case_gqa(1, 4, 1, 150, 64, "bf16", 1220, schedule=THREE)
+    check_case_gqa(1, 4, 2, 200, 128, "bf16", 1221, causal=True, schedule=THREE)
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(1, 2, 100, False), (2, 3, 300, True)])
+def test_two_pass_one_wave_schedule(B, H, N, causal):
+    check_case(B, H, N, 64, "bf16", 1230 + N, causal=causal, schedule=ONE_WAVE)
+
+
+def test_three_pass_phases_in_order_equal_the_whole():
+    import torch
+
+    import exact_second_order_fa_amd as fa
+
+    raw, _ = make_inputs(1, 2, 333, 64, 1240, "bf16")
+    t = to_device(raw, "bf16")
+    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"])
+    args = (t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"])
+    whole = fa.fa_bob(*args, schedule=THREE)
+    outs = [torch.empty_like(x) for x in whole[:4]]
+    ws = torch.empty_like(whole[4])
+    for ph in range(4):
+        fa.fa_bob(*args, gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3], ws=ws, schedule=THREE, phase=ph)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(whole, outs + [ws]):
+        n = a_.numel() if a_.dim() else 0
+        assert bool((a_.flatten()[:n] == b_.flatten()[:n]).all())
