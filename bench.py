@@ -50,6 +50,7 @@ PAGES_ABLATION = {
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bob_pass1_traffic.json")
 KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_bob.hip", "exact_second_order_fa_amd/csrc/fa_bob_ws.hip",
+                  "exact_second_order_fa_amd/csrc/fa_fwd_bwd.hip",
                   "exact_second_order_fa_amd/csrc/fa_lds.h",
                   "exact_second_order_fa_amd/csrc/fa_kernels.hip", "exact_second_order_fa_amd/csrc/fa_tile.h")
 

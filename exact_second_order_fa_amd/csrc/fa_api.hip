@@ -7,6 +7,7 @@
 #include "fa_kernels.hip"
 #include "fa_bob.hip"
 #include "fa_bob_ws.hip"
+#include "fa_fwd_bwd.hip"
 
 namespace {
 
@@ -145,7 +146,11 @@ struct Tiles {
 
 template <typename T, int D, bool C>
 void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
-  hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
+                       a);
+  else
+    hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
 }
 
 template <typename T, int D, bool C>
