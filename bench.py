@@ -106,6 +106,13 @@ class Runner:
     def fwd(self):
         self.fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], o=self.o, lse=self.lse, causal=self.w.causal)
 
+    def bwd(self):
+        t, g = self.t, self.outs
+        if not hasattr(self, "bws"):
+            self.bws = None
+        _, _, _, self.bws = self.fa.fa_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], dq=g[0], dk=g[1],
+                                           dv=g[2], ws=self.bws, causal=self.w.causal)
+
 
 def time_steps(r, steps, warmup):
     """Warmup, then `steps` timed steps.  Returns (wall ms/step, per-kernel
@@ -178,6 +185,10 @@ def cpu_baseline(w, heads):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} heads of workload {w.name} (N={w.N}, d={w.d}), full row and "
                       f"column passes in float64, {dt:.1f} s"}
+
+
+def peak_of(w):
+    return PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
 
 
 def streamed_bytes(w, schedule):
@@ -273,6 +284,14 @@ def main():
     wall, step_ev, per = time_steps(r, args.steps, args.warmup)
     bob_ms = time_plain(r.bob, args.steps)
     fwd_ms = time_plain(r.fwd, max(3, args.steps // 4))
+    bwd_ms = time_plain(r.bwd, max(3, args.steps // 4))
+    # Prerequisites ([FlashBoB] section 3): 2 N^2 d flops per contraction;
+    # forward 2 contractions, first backward 5 (S, dP, dV, dQ, dK); causal half.
+    cf = (0.5 if w.causal else 1.0) * 2.0 * w.B * w.H * w.N * w.N * w.d
+    prereq = {"fa_fwd": {"ms": round(fwd_ms, 4), "tflops": round(2 * cf / (fwd_ms * 1e9), 1),
+                         "frac_peak": round(2 * cf / (fwd_ms * 1e9) / peak_of(w), 4)},
+              "fa_bwd": {"ms": round(bwd_ms, 4), "tflops": round(5 * cf / (bwd_ms * 1e9), 1),
+                         "frac_peak": round(5 * cf / (bwd_ms * 1e9) / peak_of(w), 4)}}
     flops = w.bob_flops
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
     value = flops / (wall * 1e9)
@@ -319,6 +338,7 @@ def main():
         "kernels_ms": {"rowscalar": round(per[0], 4), "bob_pass1": round(per[1], 4),
                        "bob_pass2": round(per[2], 4), "step_events": round(step_ev, 4),
                        "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)},
+        "prerequisites": prereq,
         "sweep": sweep,
     }
     if abl_names:

@@ -119,9 +119,14 @@ unsigned grid_cols(const Ctx& c) {
   return (unsigned)(c.B * c.Hkv * ((c.N + fa::kResRows - 1) / fa::kResRows));
 }
 
-unsigned grid_rowscalar(const Ctx& c) {
+// Rows per head padded to whole 128-row blocks (the staged chain-init layout).
+int64_t padded_rows(const Ctx& c) { return (c.N + fa::kPsRows - 1) / fa::kPsRows * fa::kPsRows; }
+
+// staged: the launch also covers each head's padding rows (fa_bwd's column
+// chain inits).
+unsigned grid_rowscalar(const Ctx& c, bool staged = false) {
   const int64_t rpb = 256 / (c.d / 8);
-  return (unsigned)((c.B * c.H * c.N + rpb - 1) / rpb);
+  return (unsigned)((c.B * c.H * (staged ? padded_rows(c) : c.N) + rpb - 1) / rpb);
 }
 
 #define FA_CHECK(x)                 \
@@ -155,11 +160,21 @@ void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
 
 template <typename T, int D, bool C>
 void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
-  launch_rowscalar<T, D>(c, a, st);
-  hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
-                     a);
-  hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0,
-                     st, a);
+  if constexpr (sizeof(T) == 2) {
+    // Row scalars D plus the staged chain inits (-L/rho, -D) of the column kernel.
+    hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c, true)), dim3(256), 0, st, a);
+    constexpr int TS = D == 64 ? 128 : 64;
+    hipLaunchKernelGGL((fa::bwd_dq_dma_kernel<D, TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+    hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0, st, a);
+  } else {
+    Args b = a;
+    b.bs = nullptr;
+    launch_rowscalar<T, D>(c, b, st);
+    hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
+                       st, b);
+    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0,
+                       st, b);
+  }
 }
 
 // Schedules of the BoB ([FlashBoB] section 4.3 and appendix G.1):
@@ -267,7 +282,7 @@ const char* fa_status_str(fa_status s) {
 size_t fa_bwd_workspace_bytes(const fa_problem* p) {
   Ctx c;
   if (check_problem(p, &c) != FA_OK) return 0;
-  return (size_t)(c.B * c.H * c.N) * sizeof(float);
+  return ((size_t)(c.B * c.H * c.N) + 2 * (size_t)(c.B * c.H) * (size_t)padded_rows(c)) * sizeof(float);
 }
 
 size_t fa_bob_workspace_bytes(const fa_problem* p) {
@@ -325,6 +340,7 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
   a.r2 = desc(dv);
   a.lse = lse;
   a.D = reinterpret_cast<float*>(workspace);
+  a.bs = a.D + (size_t)(c.B * c.H * c.N);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   dispatch3<BwdL>(c, a, st);

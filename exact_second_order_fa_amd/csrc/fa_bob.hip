@@ -69,6 +69,12 @@ __device__ inline void acc_fence(f32x16 (&a)[NDB], f32x16 (&b)[NDB], f32x16 (&c)
 }
 
 template <int NDB>
+__device__ inline void acc_fence1(f32x16 (&a)[NDB]) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[db]));
+}
+
+template <int NDB>
 __device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[db]), "+a"(b[db]));

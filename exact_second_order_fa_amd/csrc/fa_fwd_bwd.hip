@@ -26,6 +26,12 @@ __device__ inline void mfma_vacc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ inline void vfence1(f32x16& a) { asm volatile("s_nop 7\n\ts_nop 4" : "+v"(a)); }
+// d = a * b (C = 0) with b resident in AGPRs.
+__device__ inline f32x16 mfma_first_a(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
 
 // ---------------------------------------------------------------------------
 // Forward: O = softmax(tau Q K^T) V with the online softmax, L = log-sum-exp.
@@ -154,6 +160,262 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int db = 0; db < NDB; ++db) store_out(o, a.r0.sn, row, N, db, [&](int idx) { return acc[db][idx] * inv; });
   if (row < N && hh == 0) a.lse_out[(int64_t)wk.bh * N + row] = kLn2 * (m + __log2f(lt));
+}
+
+// ---------------------------------------------------------------------------
+// First backward, row side: dQ = tau dS K with dS = P (dP - D).  Resident per
+// wave: q_i (scaled by pow2), do_i, L_i, D_i; streamed K, V.  Per 32-key
+// sub-tile: S^T = K Q^T and dP^T = V dO^T (keys on M), P = exp(tau S - L),
+// dS = P (dP - D), and dQ^T += K^T dS^T (transposed K from LDS).
+template <int D, int TS, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_dma_kernel(Args a) {
+  typedef SwTile<D, TS> W;
+  constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
+  constexpr int STAGE = 2 * W::BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) float kbias[TS];
+
+  const Work wk = work_item(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<bf16> q = head_of<bf16>(a.q, wk.b, wk.h), dout = head_of<bf16>(a.dout, wk.b, wk.h);
+  HeadPtr<bf16> src[2] = {head_of<bf16>(a.k, wk.b, wk.hk), head_of<bf16>(a.v, wk.b, wk.hk)};
+  const int nt = (N + TS - 1) / TS;
+  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
+  const int t_diag = CAUSAL ? wk.rb * kResRows / TS : nt;
+  const bool ragged = !CAUSAL && (N % TS) != 0;
+
+  Dma<D, TS, 2> dma;
+  dma.init(src);
+  dma.copy(0, N, lds);
+  fill_bias<TS>(kbias, (nt - 1) * TS, N);
+
+  // Resident operands in AGPRs (the matrix core reads B from there), which
+  // leaves the VGPRs to the score chains at two waves per SIMD.
+  bf16x8 qf[NKS], df[NKS];
+  load_resident<bf16, D>(qf, q.p, q.sn, row, N, a.pow2);
+  load_resident<bf16, D>(df, dout.p, dout.sn, row, N, 1.0f);
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qf[ks]), "+a"(df[ks]));
+  const int64_t rv = (int64_t)wk.bh * N;
+  const float Li = row < N ? a.lse[rv + row] : 0.0f;
+  const float Di = row < N ? a.D[rv + row] : 0.0f;
+  const float nl2 = -Li * kLog2e;
+  Reader<D, TS> rd;
+  rd.init();
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    acc[db] = zero16();
+    asm volatile("" : "+a"(acc[db]));
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): no load of the compiler's own in the loop
+
+  auto tile_body = [&](int t, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    const char* tk = lds + (t & 1) * STAGE;
+    const char* tv = tk + W::BYTES;
+    auto scores = [&](int sub, f32x16& s, f32x16& dp) {
+      if constexpr (MODE == 1) {
+        s = row_init<TS>(kbias, sub);
+      } else if constexpr (MODE == 2) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx)
+          s[idx] = (t * TS + sub * 32 + acc_pos(idx, hh) <= row) ? 0.0f : -INFINITY;
+        asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 xk = rd_row<D, TS>(tk, rd, sub, ks);
+        const bf16x8 xv = rd_row<D, TS>(tv, rd, sub, ks);
+        if (MODE == 0 && ks == 0) {
+          s = mfma_first_a(xk, qf[0]);
+        } else {
+          mfma_va(s, xk, qf[ks]);
+        }
+        if (ks == 0) {
+          dp = mfma_first_a(xv, df[0]);
+        } else {
+          mfma_va(dp, xv, df[ks]);
+        }
+      }
+    };
+    f32x16 sb[2], pb[2];
+    scores(0, sb[0], pb[0]);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      f32x16& s = sb[sub & 1];
+      f32x16& dp = pb[sub & 1];
+      asm volatile("s_nop 7\n\ts_nop 4" : "+v"(s), "+v"(dp));  // MFMA result -> VALU read
+      if (sub + 1 < NSUB) scores(sub + 1, sb[(sub + 1) & 1], pb[(sub + 1) & 1]);
+      Chain<bf16> cds;
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
+        cds.f[idx >> 3][idx & 7] = (bf16)(p * (dp[idx] - Di));
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) mfma_acc(acc[db], rd_tr<D, TS>(tk, rd, sub, db, s2), cds.f[s2]);
+    }
+  };
+  auto run = [&](int t0, int t1, auto mode_c) {
+    for (int t = t0; t < t1; ++t) {
+      dma_wait();
+      __syncthreads();
+      if (t + 1 < t_end) dma.copy((t + 1) * TS, N, lds + ((t + 1) & 1) * STAGE);
+      tile_body(t, mode_c);
+    }
+    acc_fence1<NDB>(acc);
+  };
+  if constexpr (CAUSAL) {
+    run(0, t_diag, std::integral_constant<int, 0>{});
+    run(t_diag, t_end, std::integral_constant<int, 2>{});
+  } else {
+    run(0, ragged ? nt - 1 : nt, std::integral_constant<int, 0>{});
+    if (ragged) run(nt - 1, nt, std::integral_constant<int, 1>{});
+  }
+  acc_fence1<NDB>(acc);
+  float* dq = head_out(a.r0, wk.b, wk.h);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_out(dq, a.r0.sn, row, N, db, [&](int idx) { return a.tau * acc[db][idx]; });
+}
+
+// ---------------------------------------------------------------------------
+// First backward, column side: dK = tau dS^T Q, dV = P^T dO.  Resident per
+// wave: k_j (scaled by pow2), v_j; streamed Q, dO and, per streamed row, the
+// chain inits -L/rho, -D written by the row-scalar kernel.  Per 32-row
+// sub-tile (queries on M): S = Q K^T, dP - D = dO V^T - D, P = exp(tau S - L),
+// dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  The G query heads of a
+// key/value head are streamed one after another into the same accumulators.
+template <int D, int TS, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_dma_kernel(Args a) {
+  typedef SwTile<D, TS> W;
+  constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
+  constexpr int TBYTES = 2 * W::BYTES;
+  constexpr int SBYTES = 2 * TS * 4;                       // [2][TS] floats of chain inits
+  constexpr int SROOM = SBYTES < 1024 ? 1024 : SBYTES;     // LDS room: one wave copies 1 KB
+  constexpr int STAGE = TBYTES + SROOM;
+  static_assert(kPsRows % TS == 0 && SBYTES % 512 == 0 && SBYTES <= 1024, "staged inits: one wave-wide copy");
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+
+  const Work wk = work_item_cols(a);
+  const int N = a.N;
+  const int l = lane_id(), hh = l >> 5;
+  const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
+  const HeadPtr<bf16> k = head_of<bf16>(a.k, wk.b, wk.hk), v = head_of<bf16>(a.v, wk.b, wk.hk);
+  HeadPtr<bf16> src[2] = {head_of<bf16>(a.q, wk.b, wk.h), head_of<bf16>(a.dout, wk.b, wk.h)};
+  const int64_t hstride[2] = {a.q.sh, a.dout.sh};
+  const int nt = (N + TS - 1) / TS;
+  const int64_t bs_head = (int64_t)((N + kPsRows - 1) / kPsRows) * 2 * kPsRows;  // floats per query head
+  const float* bs0 = a.bs + ((int64_t)wk.b * a.H + wk.h) * bs_head;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  Dma<D, TS, 2> dma;
+  dma.init(src, hstride);
+  // Tile t of query head h + g into dst: Q, dO and the [2][TS] inits (wave 0;
+  // lane l moves 4 floats of init e / TS, rows e % TS .., e = 4 l).
+  auto copy_tile = [&](int g, int t, const char* dst) {
+    dma.copy(t * TS, N, dst, g);
+    if (wave == 0 && l * 16 < SBYTES) {
+      const int r0 = t * TS;
+      const int e = l * 4;
+      const int kk = e / TS, rr = e % TS;
+      const float* s_ = bs0 + g * bs_head + ((int64_t)(r0 / kPsRows) * 2 + kk) * kPsRows + r0 % kPsRows + rr;
+      dma16(s_, lds_addr(dst + TBYTES));
+    }
+  };
+  const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
+  const int t_diag = CAUSAL ? (wk.rb * kResRows + kResRows + TS - 1) / TS : 0;
+  copy_tile(0, t_begin, lds);
+
+  bf16x8 kf[NKS], vf[NKS];
+  load_resident<bf16, D>(kf, k.p, k.sn, col, N, a.pow2);
+  load_resident<bf16, D>(vf, v.p, v.sn, col, N, 1.0f);
+  Reader<D, TS> rd;
+  rd.init();
+
+  f32x16 ak[NDB], av[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    ak[db] = av[db] = zero16();
+    asm volatile("" : "+a"(ak[db]), "+a"(av[db]));
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
+  auto tile_body = [&](int t, int buf, auto mode_c) {
+    constexpr int MODE = decltype(mode_c)::value;
+    const char* tq = lds + buf * STAGE;
+    const char* tdo = tq + W::BYTES;
+    const float* sc = reinterpret_cast<const float*>(tq + TBYTES);
+    auto scores = [&](int sub, f32x16& s, f32x16& dp) {
+      s = row_init<TS>(sc, sub);
+      if constexpr (MODE == 2) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx)
+          if (t * TS + sub * 32 + acc_pos(idx, hh) < col) s[idx] = -INFINITY;
+      }
+      dp = row_init<TS>(sc + TS, sub);
+      asm volatile("s_nop 1" : "+v"(s), "+v"(dp));  // VALU write -> MFMA read of C
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        mfma_v(s, rd_row<D, TS>(tq, rd, sub, ks), kf[ks]);
+        mfma_v(dp, rd_row<D, TS>(tdo, rd, sub, ks), vf[ks]);
+      }
+    };
+    f32x16 sb[2], pb[2];
+    scores(0, sb[0], pb[0]);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) {
+      f32x16& s = sb[sub & 1];
+      f32x16& dp = pb[sub & 1];
+      asm volatile("s_nop 7\n\ts_nop 4" : "+v"(s), "+v"(dp));  // MFMA result -> VALU read
+      if (sub + 1 < NSUB) scores(sub + 1, sb[(sub + 1) & 1], pb[(sub + 1) & 1]);
+      Chain<bf16> cp, cds;
+#pragma unroll
+      for (int idx = 0; idx < 16; ++idx) {
+        const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
+        cp.f[idx >> 3][idx & 7] = (bf16)p;
+        cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          mfma_acc(av[db], rd_tr<D, TS>(tdo, rd, sub, db, s2), cp.f[s2]);
+          mfma_acc(ak[db], rd_tr<D, TS>(tq, rd, sub, db, s2), cds.f[s2]);
+        }
+    }
+  };
+
+  int u = 0;  // tiles of all heads so far (picks the LDS buffer)
+  for (int g = 0; g < a.G; ++g) {
+    auto run = [&](int t0, int t1, auto mode_c) {
+      for (int t = t0; t < t1; ++t) {
+        dma_wait();
+        __syncthreads();
+        const bool wrap = t + 1 >= nt;
+        const int gn = wrap ? g + 1 : g, tn = wrap ? t_begin : t + 1;
+        if (gn < a.G) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
+        tile_body(t, u & 1, mode_c);
+        ++u;
+      }
+      acc_fence2<NDB>(ak, av);
+    };
+    if constexpr (CAUSAL) run(t_begin, min(t_diag, nt), std::integral_constant<int, 2>{});
+    run(CAUSAL ? min(t_diag, nt) : 0, nt, std::integral_constant<int, 0>{});
+  }
+  acc_fence2<NDB>(ak, av);
+  float* dk = head_out(a.r1, wk.b, wk.hk);
+  float* dv = head_out(a.r2, wk.b, wk.hk);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_out(dk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
+    store_out(dv, a.r2.sn, col, N, db, [&](int idx) { return av[db][idx]; });
+  }
 }
 
 }  // namespace fa

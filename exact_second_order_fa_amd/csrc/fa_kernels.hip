@@ -34,6 +34,7 @@ struct Args {
   float* alpha;                        // [B,H,N] BoB row scalar alpha
   float* E;                            // [B,H,N] BoB row scalar E
   float* ps;                           // [B*H][ceil(N/128)][4][128] column-pass chain inits
+  float* bs;                           // [B*H][ceil(N/128)][2][128] first-backward column chain inits (or null)
   int B, H, N;
   int Hk, G;                 // key/value heads and query heads per key/value head (H = Hk * G)
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
@@ -164,13 +165,17 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void rowscalar_kernel(Args a) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
-  const int64_t total = (int64_t)a.B * a.H * a.N;
+  // With a.bs the launch also covers the padding rows of each head's last
+  // 128-row block, which get the masking inits (-inf, 0).
+  const int NP = a.bs ? (a.N + kPsRows - 1) / kPsRows * kPsRows : a.N;
+  const int64_t total = (int64_t)a.B * a.H * NP;
   const int64_t gr = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int c0 = (threadIdx.x % LPR) * 8;
+  const int64_t bh = gr / NP;
+  const int i = (int)(gr % NP);
+  const bool valid = gr < total && i < a.N;
   float acc = 0.0f;
-  if (gr < total) {
-    const int64_t bh = gr / a.N;
-    const int i = (int)(gr % a.N);
+  if (valid) {
     const int b = (int)(bh / a.H), h = (int)(bh % a.H);
     const HeadPtr<T> dout = head_of<T>(a.dout, b, h);
     const HeadPtr<float> o = head_of<float>(a.o, b, h);
@@ -199,7 +204,16 @@ __global__ __launch_bounds__(256) void rowscalar_kernel(Args a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (gr < total && (threadIdx.x % LPR) == 0) a.D[gr] = acc;
+  if (gr < total && (threadIdx.x % LPR) == 0) {
+    const int64_t rv = bh * a.N + i;
+    if (valid) a.D[rv] = acc;
+    if (a.bs) {
+      // Chain inits of the first-backward column pass: -L/rho, -D.
+      float* st = a.bs + (bh * (NP / kPsRows) + i / kPsRows) * 2 * kPsRows + i % kPsRows;
+      st[0] = valid ? -a.lse[rv] / a.rho : -INFINITY;
+      st[kPsRows] = valid ? -acc : 0.0f;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

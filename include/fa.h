@@ -106,7 +106,9 @@ const char* fa_status_str(fa_status s);
 fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
                  fa_tensor o, float* lse, void* stream);
 
-/* Workspace bytes fa_bwd needs: the row vector D, B*H*N fp32. */
+/* Workspace bytes fa_bwd needs: the row vector D (B*H*N fp32, first), then
+ * 8 * B*H*ceil(N/128)*128 bytes of per-row chain inits for the key-side
+ * kernel (an internal layout). */
 size_t fa_bwd_workspace_bytes(const fa_problem* p);
 
 /*
@@ -114,7 +116,7 @@ size_t fa_bwd_workspace_bytes(const fa_problem* p);
  *   dP = dO V^T, dV = P^T dO, dS_ij = P_ij (dP_ij - D_i),
  *   dQ = tau dS K, dK = tau dS^T Q,
  * with D_i = rowsum(dO * O)_i ([FA2-recompute]), computed by a row-scalar
- * kernel into the workspace (first B*H*N floats).
+ * kernel into the workspace (first B*H*N floats; the rest is internal).
  * In:  q, k, v, dout (in_dtype); o (fp32) and lse (fp32) from fa_fwd.
  * Out: dq (H heads), dk, dv (H_kv heads: sums over each group) in fp32.
  * Deterministic: every output block has one writer.

@@ -79,7 +79,8 @@ def test_workspace_sizes(lib):
         lib.fa_bob_workspace_bytes(ctypes.byref(p))
     # D, alpha, E ([B,H,N] fp32 each), then four chain inits per row padded to 128 rows
     assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == (3 * 2 * 3 * 130 + 4 * 2 * 3 * 256) * 4
-    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == 2 * 3 * 130 * 4
+    # D ([B,H,N] fp32), then two chain inits per row padded to 128 rows
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == (2 * 3 * 130 + 2 * 2 * 3 * 256) * 4
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(d=96))) == 0
     assert lib.fa_bob_workspace_bytes(None) == 0
 
