@@ -188,7 +188,8 @@ template <typename T, int D, bool RHO1, bool C>
 void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int phase) {
   const dim3 g(grid_rows(c)), b(fa::kThreads), gc(grid_cols(c));
   auto want = [&](int ph) { return phase < 0 || phase == ph; };
-  if (want(0)) launch_rowscalar<T, D>(c, a, st);
+  // The bf16 two-pass row passes compute D themselves; phase 0 then launches nothing.
+  if (want(0) && !(sizeof(T) == 2 && schedule != 2)) launch_rowscalar<T, D>(c, a, st);
   const int col_phase = schedule == 2 ? 3 : 2;
   if constexpr (sizeof(T) == 2) {
     if (schedule == 2) {

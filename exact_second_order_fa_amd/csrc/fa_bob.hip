@@ -68,6 +68,30 @@ __device__ inline void acc_fence(f32x16 (&a)[NDB], f32x16 (&b)[NDB], f32x16 (&c)
     asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[db]), "+a"(b[db]), "+a"(c[db]), "+a"(d[db]));
 }
 
+// D_i = rowsum(dO * O)_i ([FA2-recompute]) of this lane's resident row, from
+// its resident bf16 dO operands (k-step ks holds d-columns 16 ks + 8 hh ..
+// + 7) and the matching fp32 O values; the two halves of the wave hold the
+// two halves of the row.
+template <int D>
+__device__ inline float resident_rowdot(const bf16x8 (&df)[D / 16], const HeadPtr<float>& o, int row, int N) {
+  const int hh = lane_id() >> 5;
+  float acc = 0.0f;
+  if (row < N) {
+    const float* orow = o.p + (int64_t)row * o.sn + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(orow + 16 * ks);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf((float)df[ks][e], x0[e], acc);
+        acc = fmaf((float)df[ks][e + 4], x1[e], acc);
+      }
+    }
+  }
+  return half_sum(acc);
+}
+
 template <int NDB>
 __device__ inline void acc_fence1(f32x16 (&a)[NDB]) {
 #pragma unroll
@@ -115,7 +139,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float kbias[TS];  // chain init of a ragged last tile
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
@@ -142,7 +166,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   load_resident<bf16, D>(df, dout.p, dout.sn, row, N, 1.0f);
   const int64_t rv = (int64_t)wk.bh * N;
   const float Li = row < N ? a.lse[rv + row] : 0.0f;
-  const float Di = row < N ? a.D[rv + row] : 0.0f;
+  // Two-pass: D is computed here (no separate row-scalar kernel) and written
+  // for the column pass; the three-pass row sweep reads the row-scalar kernel's.
+  const float Di = SCHED == 0 ? resident_rowdot<D>(df, head_of<float>(a.o, wk.b, wk.h), row, N)
+                              : (row < N ? a.D[rv + row] : 0.0f);
   const float nl2 = -Li * kLog2e;
   const float Ai = (SCHED == 1 && row < N) ? a.alpha[rv + row] : 0.0f;  // known alpha (three-pass)
 
@@ -327,7 +354,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float eo = SCHED == 0 ? esum : esum + Ai * Di;  // E° = E + alpha D
   const float eob = half_sum(eob_p);
   if (row < N && hh == 0) {
-    if constexpr (SCHED == 0) a.alpha[rv + row] = alpha;
+    if constexpr (SCHED == 0) {
+      a.alpha[rv + row] = alpha;
+      a.D[rv + row] = Di;
+    }
     a.E[rv + row] = SCHED == 0 ? eo - alpha * Di : esum;
   }
   if (hh == 0) {
@@ -384,7 +414,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float kbias[TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);

@@ -134,7 +134,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int nblk = (a.N + kResRows - 1) / kResRows;
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wid / nblk, rb = wid % nblk, bb = bh / a.H, hd = bh % a.H, hk = hd / a.G;
+  // Causal: the largest row blocks of a head first (see work_item).
+  const int bh = wid / nblk, rb = CAUSAL ? nblk - 1 - wid % nblk : wid % nblk, bb = bh / a.H, hd = bh % a.H,
+            hk = hd / a.G;
   const int N = a.N;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool producer = wave < 4;
@@ -184,7 +186,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     load_resident<bf16, D>(uqf, uq.p, uq.sn, row, N, a.pow2);
     load_resident<bf16, D>(df, dout.p, dout.sn, row, N, 1.0f);
     const float Li = row < N ? a.lse[rv + row] : 0.0f;
-    const float Di = row < N ? a.D[rv + row] : 0.0f;
+    // D = rowsum(dO * O) of this row, computed here and written for the column pass.
+    const float Di = resident_rowdot<D>(df, head_of<float>(a.o, bb, hd), row, N);
     const float nl2 = -Li * kLog2e;
     // eob_p: E° summed from the bf16-rounded products P t0 that the matrix core
     // accumulates into Omega.  gQ = tau (Omega - alpha R' - E° B) uses it, so the
@@ -354,6 +357,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (row < N) {
         a.alpha[rv + row] = alpha;
         a.E[rv + row] = eo - alpha * Di;
+        a.D[rv + row] = Di;
       }
       // Chain inits of the column pass (see bob_pass2_dma_kernel).
       float* ps = a.ps + ((int64_t)bh * nblk + row / kPsRows) * 4 * kPsRows + row % kPsRows;

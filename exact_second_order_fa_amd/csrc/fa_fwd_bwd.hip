@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float kbias[TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float kbias[TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);

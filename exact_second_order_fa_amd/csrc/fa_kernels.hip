@@ -63,12 +63,15 @@ struct Work {
   int bh, b, h, hk, rb;
 };
 
-__device__ inline Work work_item(const Args& a) {
+// heavy_first: causal row-side kernels do work proportional to rb + 1; the
+// blocks of a head are taken in descending rb so the largest ones start
+// first and the last wave of workgroups is made of the small ones.
+__device__ inline Work work_item(const Args& a, bool heavy_first = false) {
   const int nblk = (a.N + kResRows - 1) / kResRows;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   Work r;
   r.bh = w / nblk;
-  r.rb = w % nblk;
+  r.rb = heavy_first ? nblk - 1 - w % nblk : w % nblk;
   r.b = r.bh / a.H;
   r.h = r.bh % a.H;
   r.hk = r.h / a.G;
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float kbias[2][TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float kbias[2][TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][4 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float kbias[2][TS];
 
-  const Work wk = work_item(a);
+  const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int row = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);

@@ -143,9 +143,10 @@ size_t fa_bob_workspace_bytes(const fa_problem* p);
  *   d~S = P (d~P - E),  h = F - alpha,
  *   gq  = tau (d~S K + dS U_K),     gk  = tau (d~S^T Q + dS^T U_Q),
  *   gv  = (P h)^T dO,               gdo = P U_V + (P h) V.
- * Schedule ([FlashBoB] section 4.3): a row-scalar kernel writes D; a
- * row-major pass accumulates the row outputs with the affine corrections of
- * section 4.2 and writes gq, gdo, alpha, E once per row block; a
+ * Schedule ([FlashBoB] section 4.3): D = rowsum(dO * O) (computed inside the
+ * row pass for bf16 inputs, by a row-scalar kernel for fp32); a row-major
+ * pass accumulates the row outputs with the affine corrections of section 4.2
+ * and writes gq, gdo, alpha, E (and D) once per row block; a
  * column-major pass writes gk, gv once per column block.  No N x N tensor is
  * written anywhere and no atomics are used, so results are deterministic.
  * In:  q, k, v, dout, uq, uk, uv (in_dtype); o (fp32), lse (fp32) from fa_fwd;
@@ -164,8 +165,9 @@ fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
 /*
  * fa_bob_phase -- one kernel of fa_bob, for per-kernel timing and profiling.
  * Same arguments as fa_bob plus `phase`: 0 launches the row-scalar kernel
- * (writes D), 1 the row-major pass (reads D; writes gq, gdo, alpha, E), 2 the
- * column-major pass (reads D, alpha, E; writes gk, gv).  Calling phases 0, 1,
+ * (writes D; with bf16 inputs the row pass computes D itself and phase 0
+ * launches nothing), 1 the row-major pass (writes gq, gdo, alpha, E and, for
+ * bf16, D), 2 the column-major pass (reads D, alpha, E; writes gk, gv).  Calling phases 0, 1,
  * 2 in that order on one stream is exactly fa_bob.  A phase outside 0..2
  * returns FA_ERR_UNSUPPORTED.
  */
@@ -188,9 +190,9 @@ typedef enum fa_schedule {
  * ablation of [FlashBoB] appendix G.1 ("Three-pass versus two-pass").  Every
  * schedule computes the same outputs and workspace values (D, alpha, E) up to
  * rounding; they differ in how many sweeps stream the key side:
- *   FA_SCHED_TWO_PASS, FA_SCHED_TWO_PASS_1WAVE: phases 0 (row scalars D), 1
- *     (row pass: gq, gdo, alpha, E with the affine corrections of section 4.2),
- *     2 (column pass: gk, gv);
+ *   FA_SCHED_TWO_PASS, FA_SCHED_TWO_PASS_1WAVE: phases 0 (row scalars D; bf16:
+ *     nothing, the row pass computes D), 1 (row pass: gq, gdo, alpha, E with
+ *     the affine corrections of section 4.2), 2 (column pass: gk, gv);
  *   FA_SCHED_THREE_PASS: phases 0 (D), 1 (alpha-only row sweep, streams K and
  *     U_K), 2 (row pass with alpha known: gq by the delayed E-correction, gdo,
  *     E), 3 (column pass).
