@@ -123,10 +123,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int NSTAGE = 5;
   constexpr int STAGE = 4 * W::BYTES;    // 16 KB
   constexpr int OPB = 4 * 2 * 64 * 16;   // operands of one wave and tile: 8 KB
-  // Operand buffer of a wave: word w (0..7) of chain k (P, P F, P P~, dS) of
-  // every lane, lane-contiguous ([k][w][lane] words), so that the producer's
-  // one-word writes and the consumer's word reads are free of bank conflicts.
-  auto op_off = [](int k, int w) { return (k * 8 + w) * 256; };
+  // Operand buffer of a wave: word w (0..7) of the four chains (P, P F, P P~,
+  // dS) of a lane as one 16-byte group, lane-contiguous ([w][lane][k] words):
+  // the producer writes the four words of an element pair with one 128-bit
+  // store and the consumer reads four of them with one 128-bit load, both
+  // free of bank conflicts.
+  auto op_off = [](int w) { return w * 64 * 16; };
   static_assert(NSTAGE * STAGE <= (int)kStageMask + 1, "stage region larger than its offset mask");
   __shared__ __attribute__((aligned(1024))) char stages[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(1024))) char ops[2][4 * OPB];
@@ -197,8 +199,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float alpha_p = 0.0f, eo_p = 0.0f, eob_p = 0.0f;
     rd.init();
     f32x16 S[2], F[2], DP[2], C[2];  // score chains, double buffered across slots
-    const lds_p ob0 = (lds_p)ops[0] + wi * OPB + 4 * l;  // this wave's operand buffers
-    const lds_p ob1 = (lds_p)ops[1] + wi * OPB + 4 * l;
+    const lds_p ob0 = (lds_p)ops[0] + wi * OPB + 16 * l;  // this wave's operand buffers
+    const lds_p ob1 = (lds_p)ops[1] + wi * OPB + 16 * l;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // the compiler's own loads are done before the loop
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -293,11 +295,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                        wds = pack_bf16(pair[3], ds);
         add_here(eob_p, __builtin_bit_cast(float, wpt << 16));
         add_here(eob_p, __builtin_bit_cast(float, wpt & 0xffff0000u));
-        typedef __attribute__((address_space(3))) uint32_t* wptr;
-        *reinterpret_cast<wptr>(obuf + op_off(0, w)) = wp;
-        *reinterpret_cast<wptr>(obuf + op_off(1, w)) = wpf;
-        *reinterpret_cast<wptr>(obuf + op_off(2, w)) = wpt;
-        *reinterpret_cast<wptr>(obuf + op_off(3, w)) = wds;
+        typedef __attribute__((address_space(3))) u32x4* wptr;
+        const u32x4 words = {wp, wpf, wpt, wds};
+        *reinterpret_cast<wptr>(obuf + op_off(w)) = words;
       }
     };
     // Slot sl in 1 .. nt - 1: scores of tile sl into set P, elementwise of
@@ -374,8 +374,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 ag[NDB], aom[NDB], ar[NDB], abk[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) ag[db] = aom[db] = ar[db] = abk[db] = zero16();
-    const lds_cp ob0 = (lds_cp)ops[0] + wi * OPB + 4 * l;
-    const lds_cp ob1 = (lds_cp)ops[1] + wi * OPB + 4 * l;
+    const lds_cp ob0 = (lds_cp)ops[0] + wi * OPB + 16 * l;
+    const lds_cp ob1 = (lds_cp)ops[1] + wi * OPB + 16 * l;
     rd.init();
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -403,12 +403,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const lds_cp o = (kt & 1) ? ob1 : ob0;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          // B operand of chain k: words 4 s2 .. 4 s2 + 3 (keys 16 s2 + 8 hh ..).
-          auto opnd = [&](int k) {
-            typedef const __attribute__((address_space(3))) uint32_t* rp;
-            u32x4 v;
+          // B operand of chain k: words 4 s2 .. 4 s2 + 3 (keys 16 s2 + 8 hh ..),
+          // word k of the groups 4 s2 + j.
+          typedef const __attribute__((address_space(3))) u32x4* rp;
+          u32x4 grp[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = *reinterpret_cast<rp>(o + op_off(k, 4 * s2 + j));
+          for (int j = 0; j < 4; ++j) grp[j] = *reinterpret_cast<rp>(o + op_off(4 * s2 + j));
+          auto opnd = [&](int k) {
+            const u32x4 v = {grp[0][k], grp[1][k], grp[2][k], grp[3][k]};
             return __builtin_bit_cast(bf16x8, v);
           };
           const bf16x8 bp = opnd(0), bpf = opnd(1), bpt = opnd(2), bds = opnd(3);
