@@ -648,6 +648,108 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
 
+    // Woven schedule (d = 64, one wave per SIMD): the elementwise work of
+    // sub-tile sub is spread over the score MFMAs of sub-tile sub + 1 and the
+    // accumulation MFMAs of sub-tile sub - 1 (one element after every two
+    // MFMAs, held in place by scheduling barriers), so that the VALU works
+    // while the matrix core does.  Score sets and operand chains alternate
+    // between two register sets by sub-tile parity.
+    auto woven = [&]() {
+      f32x16 cs[2][4];        // [set][S, F, dP, C]
+      Chain<bf16> ch[2][3];   // [set][P x, P dP, P h]
+      // Score MFMAs of sub-tile sub into set z; hook(i) after MFMA i (0..19).
+      // The A operands of k-step ks + 1 are read right after the last MFMA of
+      // k-step ks that uses their registers.
+      auto scores_w = [&](int sub, f32x16 (&z)[4], auto&& hook) {
+        z[0] = row_init<TS>(sc, sub);
+        if constexpr (MODE == 2) {
+#pragma unroll
+          for (int idx = 0; idx < 16; ++idx)
+            if (t * TS + sub * 32 + acc_pos(idx, hh) < col) z[0][idx] = -INFINITY;
+          asm volatile("s_nop 1" : "+v"(z[0]));  // VALU write -> MFMA read of C
+        }
+        z[2] = row_init<TS>(sc + TS, sub);
+        z[1] = row_init<TS>(sc + 2 * TS, sub);
+        z[3] = row_init<TS>(sc + 3 * TS, sub);
+        bf16x8 xq = rd_row<D, TS>(tq, rd, sub, 0), xuq = rd_row<D, TS>(tuq, rd, sub, 0),
+               xd = rd_row<D, TS>(tdo, rd, sub, 0);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bool more = ks + 1 < NKS;
+          mfma_v(z[0], xq, kf[ks]);
+          hook(5 * ks);
+          mfma_v(z[1], xuq, kf[ks]);
+          if (more) xuq = rd_row<D, TS>(tuq, rd, sub, ks + 1);
+          hook(5 * ks + 1);
+          mfma_v(z[1], xq, ukf[ks]);
+          if (more) xq = rd_row<D, TS>(tq, rd, sub, ks + 1);
+          hook(5 * ks + 2);
+          if constexpr (RESA) {
+            mfma_va(z[2], xd, vf[ks]);
+            hook(5 * ks + 3);
+            mfma_va(z[3], xd, uvf[ks]);
+          } else {
+            mfma_v(z[2], xd, vf[ks]);
+            hook(5 * ks + 3);
+            mfma_v(z[3], xd, uvf[ks]);
+          }
+          if (more) xd = rd_row<D, TS>(tdo, rd, sub, ks + 1);
+          hook(5 * ks + 4);
+        }
+      };
+      // Accumulation MFMAs of sub-tile sub from chains c; hook(i) after MFMA
+      // i (0..3 NSLICE - 1).
+      auto acc_w = [&](int sub, const Chain<bf16> (&c)[3], auto&& hook) {
+        bf16x8 xq = rd_tr<D, TS>(tq, rd, sub, 0, 0), xuq = rd_tr<D, TS>(tuq, rd, sub, 0, 0),
+               xd = rd_tr<D, TS>(tdo, rd, sub, 0, 0);
+#pragma unroll
+        for (int sl = 0; sl < NSLICE; ++sl) {
+          const int db = sl >> 1, s2 = sl & 1, nd = (sl + 1) >> 1, ns = (sl + 1) & 1;
+          const bool more = sl + 1 < NSLICE;
+          mfma_acc(ak[db], xq, c[0].f[s2]);
+          if (more) xq = rd_tr<D, TS>(tq, rd, sub, nd, ns);
+          hook(3 * sl);
+          mfma_acc(ak[db], xuq, c[1].f[s2]);
+          if (more) xuq = rd_tr<D, TS>(tuq, rd, sub, nd, ns);
+          hook(3 * sl + 1);
+          mfma_acc(av[db], xd, c[2].f[s2]);
+          if (more) xd = rd_tr<D, TS>(tdo, rd, sub, nd, ns);
+          hook(3 * sl + 2);
+        }
+      };
+      auto element = [&](const f32x16 (&z)[4], int idx, Chain<bf16> (&c)[3]) {
+        const float p = __builtin_amdgcn_exp2f(z[0][idx] * a.c1);
+        const float h = RHO1 ? z[1][idx] : z[1][idx] * a.rho;
+        const float x = fmaf(h, z[2][idx], z[3][idx]);
+        c[0].f[idx >> 3][idx & 7] = (bf16)(p * x);
+        c[1].f[idx >> 3][idx & 7] = (bf16)(p * z[2][idx]);
+        c[2].f[idx >> 3][idx & 7] = (bf16)(p * h);
+      };
+
+      scores_w(0, cs[0], [](int) {});
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        const int P = sub & 1, Q = P ^ 1;
+        mfma_fence(cs[P][0], cs[P][1], cs[P][2], cs[P][3]);
+        const int NS = sub + 1 < NSUB ? 20 : 0, M = NS + (sub > 0 ? 3 * NSLICE : 0);
+        // Elements [16 i / M, 16 (i + 1) / M) after MFMA i.
+        auto hook = [&](int i) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int e = 16 * i / M; e < 16 * (i + 1) / M; ++e) element(cs[P], e, ch[P]);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        if (sub + 1 < NSUB) scores_w(sub + 1, cs[Q], hook);
+        if (sub > 0) acc_w(sub - 1, ch[Q], [&](int i) { hook(NS + i); });
+        if (M == 0) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) element(cs[P], e, ch[P]);
+        }
+      }
+      acc_w(NSUB - 1, ch[(NSUB - 1) & 1], [](int) {});
+    };
+
+    if constexpr (SPLIT) {
     f32x16 s, f, dp, c;
     scores(0, s, f, dp, c);
     Chain<bf16> pdt, pds, pw;  // chains of the previous sub-tile
@@ -669,10 +771,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int db = (part - 2) * H; db < (part - 1) * H; ++db) acc_slice(sub, db, 0, cdt, cds, cw);
           }
-        } else if (sub > 0) {
-#pragma unroll
-          for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl)
-            acc_slice(sub - 1, sl >> 1, sl & 1, pdt, pds, pw);
         }
       }
       pdt = cdt;
@@ -680,12 +778,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       pw = cw;
       if (sub + 1 < NSUB) scores(sub + 1, s, f, dp, c);
     }
-    if constexpr (SPLIT) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_slice(NSUB - 1, db, 1, pdt, pds, pw);
+    for (int db = 0; db < NDB; ++db) acc_slice(NSUB - 1, db, 1, pdt, pds, pw);
     } else {
-#pragma unroll
-      for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pdt, pds, pw);
+      woven();
     }
   };
 
