@@ -15,6 +15,7 @@
 #include <type_traits>
 
 #include "fa_lds.h"
+#include <utility>
 
 namespace fa {
 
@@ -38,6 +39,17 @@ __device__ inline void fill_bias(float* b, int row0, int N) {
 //   * an MFMA reading a VGPR as C -> a VALU write of it: 7 (C is always the
 //     tied destination here, so the fence above covers it);
 //   * back-to-back accumulation into the same registers needs none.
+
+// f(integral_constant<int, i>) for i = B .. E - 1, in order: the index is a
+// compile-time constant inside f, whatever the unroller decides.
+template <int B, int... I, typename F>
+__device__ inline void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, B + I>{}), ...);
+}
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (E > B) static_for_impl<B>(std::make_integer_sequence<int, E - B>{}, f);
+}
 
 // d = a * b (a chain start; C = 0).
 __device__ inline f32x16 mfma_first(bf16x8 a, bf16x8 b) {
@@ -574,6 +586,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(vf[ks]), "+a"(uvf[ks]));
   }
+  if constexpr (!SPLIT) {
+    // The woven schedule reads every resident operand from AGPRs, so that
+    // the compiler has no reason to copy one into VGPRs in front of an MFMA.
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(ukf[ks]), "+a"(vf[ks]), "+a"(uvf[ks]));
+  }
 
   Reader<D, TS> rd;
   rd.init();
@@ -648,105 +666,203 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
 
-    // Woven schedule (d = 64, one wave per SIMD): the elementwise work of
-    // sub-tile sub is spread over the score MFMAs of sub-tile sub + 1 and the
-    // accumulation MFMAs of sub-tile sub - 1 (one element after every two
-    // MFMAs, held in place by scheduling barriers), so that the VALU works
-    // while the matrix core does.  Score sets and operand chains alternate
-    // between two register sets by sub-tile parity.
+    // Woven schedule (d = 64, one wave per SIMD).  The wave issues in order,
+    // so the matrix core only stays busy if the work between two MFMAs takes
+    // no longer than one MFMA (32 cycles).  Per sub-tile sub the MFMAs are
+    // the accumulations of sub-tile sub - 1 (12) and then the scores of
+    // sub-tile sub + 1 (20); the elementwise work of sub-tile sub is cut into
+    // 32 parts of at most six VALU instructions, one after each MFMA:
+    //   E(e)  P of element e (one exp),
+    //   A(j)  the P x chain of element pair j,
+    //   B(j)  the P dP and P h chains of pair j,
+    // in the order E0..E3, then A(j) B(j) E(2j+4) E(2j+5) for j = 0..5, then
+    // A6 B6 A7 B7, so that every exp has two slots to finish before its P is
+    // used.  Scheduling barriers hold this order.  The LDS operands of an MFMA
+    // are loaded at least three MFMAs ahead: the transposed operands of the
+    // accumulations two slices ahead (across sub-tiles), the score rows one
+    // k-step ahead, and the chain inits of sub-tile sub + 1 during the
+    // accumulations.  Score sets and operand chains alternate between two
+    // register sets by sub-tile parity.
     auto woven = [&]() {
       f32x16 cs[2][4];        // [set][S, F, dP, C]
       Chain<bf16> ch[2][3];   // [set][P x, P dP, P h]
-      // Score MFMAs of sub-tile sub into set z; hook(i) after MFMA i (0..19).
-      // The A operands of k-step ks + 1 are read right after the last MFMA of
-      // k-step ks that uses their registers.
-      auto scores_w = [&](int sub, f32x16 (&z)[4], auto&& hook) {
-        z[0] = row_init<TS>(sc, sub);
+      float pv[16];           // P of the sub-tile in work
+      bf16x8 ta[2][3];        // transposed operands of two slices: [slice & 1][Q, U_Q, dO]
+      bf16x8 xr[3];           // score operands of one k-step: [Q, U_Q, dO]
+
+      // Transposed operand k of slice sl (d-block sl % NDB, half sl / NDB) of
+      // sub-tile sub into ta[sl & 1][k].
+      auto load_tr = [&](int sub, int sl, int k) {
+        const char* tile = k == 0 ? tq : (k == 1 ? tuq : tdo);
+        ta[sl & 1][k] = rd_tr<D, TS>(tile, rd, sub, sl % NDB, sl / NDB);
+      };
+      auto load_row = [&](int sub, int ks, int k) {
+        const char* tile = k == 0 ? tq : (k == 1 ? tuq : tdo);
+        xr[k] = rd_row<D, TS>(tile, rd, sub, ks);
+      };
+      // Chain init c (0 S, 1 F, 2 dP, 3 C) of sub-tile sub into z.
+      auto load_init = [&](int sub, f32x16 (&z)[4], int c) {
+        z[c] = row_init<TS>(sc + (c == 0 ? 0 : c == 1 ? 2 * TS : c == 2 ? TS : 3 * TS), sub);
+      };
+      auto mask_init = [&](int sub, f32x16 (&z)[4]) {
         if constexpr (MODE == 2) {
 #pragma unroll
           for (int idx = 0; idx < 16; ++idx)
             if (t * TS + sub * 32 + acc_pos(idx, hh) < col) z[0][idx] = -INFINITY;
           asm volatile("s_nop 1" : "+v"(z[0]));  // VALU write -> MFMA read of C
         }
-        z[2] = row_init<TS>(sc + TS, sub);
-        z[1] = row_init<TS>(sc + 2 * TS, sub);
-        z[3] = row_init<TS>(sc + 3 * TS, sub);
-        bf16x8 xq = rd_row<D, TS>(tq, rd, sub, 0), xuq = rd_row<D, TS>(tuq, rd, sub, 0),
-               xd = rd_row<D, TS>(tdo, rd, sub, 0);
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bool more = ks + 1 < NKS;
-          mfma_v(z[0], xq, kf[ks]);
-          hook(5 * ks);
-          mfma_v(z[1], xuq, kf[ks]);
-          if (more) xuq = rd_row<D, TS>(tuq, rd, sub, ks + 1);
-          hook(5 * ks + 1);
-          mfma_v(z[1], xq, ukf[ks]);
-          if (more) xq = rd_row<D, TS>(tq, rd, sub, ks + 1);
-          hook(5 * ks + 2);
-          if constexpr (RESA) {
-            mfma_va(z[2], xd, vf[ks]);
-            hook(5 * ks + 3);
-            mfma_va(z[3], xd, uvf[ks]);
-          } else {
-            mfma_v(z[2], xd, vf[ks]);
-            hook(5 * ks + 3);
-            mfma_v(z[3], xd, uvf[ks]);
-          }
-          if (more) xd = rd_row<D, TS>(tdo, rd, sub, ks + 1);
-          hook(5 * ks + 4);
-        }
-      };
-      // Accumulation MFMAs of sub-tile sub from chains c; hook(i) after MFMA
-      // i (0..3 NSLICE - 1).
-      auto acc_w = [&](int sub, const Chain<bf16> (&c)[3], auto&& hook) {
-        bf16x8 xq = rd_tr<D, TS>(tq, rd, sub, 0, 0), xuq = rd_tr<D, TS>(tuq, rd, sub, 0, 0),
-               xd = rd_tr<D, TS>(tdo, rd, sub, 0, 0);
-#pragma unroll
-        for (int sl = 0; sl < NSLICE; ++sl) {
-          const int db = sl >> 1, s2 = sl & 1, nd = (sl + 1) >> 1, ns = (sl + 1) & 1;
-          const bool more = sl + 1 < NSLICE;
-          mfma_acc(ak[db], xq, c[0].f[s2]);
-          if (more) xq = rd_tr<D, TS>(tq, rd, sub, nd, ns);
-          hook(3 * sl);
-          mfma_acc(ak[db], xuq, c[1].f[s2]);
-          if (more) xuq = rd_tr<D, TS>(tuq, rd, sub, nd, ns);
-          hook(3 * sl + 1);
-          mfma_acc(av[db], xd, c[2].f[s2]);
-          if (more) xd = rd_tr<D, TS>(tdo, rd, sub, nd, ns);
-          hook(3 * sl + 2);
-        }
-      };
-      auto element = [&](const f32x16 (&z)[4], int idx, Chain<bf16> (&c)[3]) {
-        const float p = __builtin_amdgcn_exp2f(z[0][idx] * a.c1);
-        const float h = RHO1 ? z[1][idx] : z[1][idx] * a.rho;
-        const float x = fmaf(h, z[2][idx], z[3][idx]);
-        c[0].f[idx >> 3][idx & 7] = (bf16)(p * x);
-        c[1].f[idx >> 3][idx & 7] = (bf16)(p * z[2][idx]);
-        c[2].f[idx >> 3][idx & 7] = (bf16)(p * h);
       };
 
-      scores_w(0, cs[0], [](int) {});
-#pragma unroll
-      for (int sub = 0; sub < NSUB; ++sub) {
-        const int P = sub & 1, Q = P ^ 1;
+      // Elementwise part Q (0..31) of the sub-tile in set z / chains c.
+      auto part = [&](const f32x16 (&z)[4], Chain<bf16> (&c)[3], auto qc) {
+        constexpr int q = decltype(qc)::value;
+        auto E = [&](auto ec) {
+          constexpr int e = decltype(ec)::value;
+          pv[e] = __builtin_amdgcn_exp2f(z[0][e] * a.c1);
+        };
+        auto hv = [&](int e) { return RHO1 ? z[1][e] : z[1][e] * a.rho; };
+        auto A = [&](auto jc) {
+          constexpr int e0 = 2 * decltype(jc)::value, e1 = e0 + 1;
+          c[0].f[e0 >> 3][e0 & 7] = (bf16)(pv[e0] * fmaf(hv(e0), z[2][e0], z[3][e0]));
+          c[0].f[e1 >> 3][e1 & 7] = (bf16)(pv[e1] * fmaf(hv(e1), z[2][e1], z[3][e1]));
+        };
+        auto Bc = [&](auto jc) {
+          constexpr int e0 = 2 * decltype(jc)::value, e1 = e0 + 1;
+          c[1].f[e0 >> 3][e0 & 7] = (bf16)(pv[e0] * z[2][e0]);
+          c[1].f[e1 >> 3][e1 & 7] = (bf16)(pv[e1] * z[2][e1]);
+          c[2].f[e0 >> 3][e0 & 7] = (bf16)(pv[e0] * hv(e0));
+          c[2].f[e1 >> 3][e1 & 7] = (bf16)(pv[e1] * hv(e1));
+        };
+        if constexpr (q < 4) {
+          E(std::integral_constant<int, q>{});
+        } else if constexpr (q < 28) {
+          constexpr int j = (q - 4) >> 2, r = (q - 4) & 3;
+          if constexpr (r == 0) A(std::integral_constant<int, j>{});
+          else if constexpr (r == 1) Bc(std::integral_constant<int, j>{});
+          else E(std::integral_constant<int, 2 * j + 2 + r>{});
+        } else {
+          constexpr int j = 6 + ((q - 28) >> 1);
+          if constexpr ((q & 1) == 0) A(std::integral_constant<int, j>{});
+          else Bc(std::integral_constant<int, j>{});
+        }
+      };
+
+      // One sub-tile iteration: MFMAs of acc(sub - 1) then scores(sub + 1),
+      // elementwise parts of sub after them (PRE parts before the first MFMA
+      // when there is no accumulation, to cover the first loads).
+      auto iteration = [&](auto subc) {
+        constexpr int sub = decltype(subc)::value;
+        constexpr int P = sub & 1, Q = P ^ 1;
+        constexpr bool has_acc = sub > 0, has_sc = sub + 1 < NSUB;
+        constexpr int NA = has_acc ? 3 * NSLICE : 0, NSC = has_sc ? 5 * NKS : 0;
+        constexpr int PRE = has_acc ? 0 : 4, M = NA + NSC;
         mfma_fence(cs[P][0], cs[P][1], cs[P][2], cs[P][3]);
-        const int NS = sub + 1 < NSUB ? 20 : 0, M = NS + (sub > 0 ? 3 * NSLICE : 0);
-        // Elements [16 i / M, 16 (i + 1) / M) after MFMA i.
-        auto hook = [&](int i) {
+        auto run_parts = [&](auto q0c, auto q1c) {
           __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int e = 16 * i / M; e < 16 * (i + 1) / M; ++e) element(cs[P], e, ch[P]);
+          static_for<decltype(q0c)::value, decltype(q1c)::value>([&](auto qc) { part(cs[P], ch[P], qc); });
           __builtin_amdgcn_sched_barrier(0);
         };
-        if (sub + 1 < NSUB) scores_w(sub + 1, cs[Q], hook);
-        if (sub > 0) acc_w(sub - 1, ch[Q], [&](int i) { hook(NS + i); });
-        if (M == 0) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) element(cs[P], e, ch[P]);
+        // Parts after MFMA I of this iteration.
+        auto after = [&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          run_parts(std::integral_constant<int, PRE + (32 - PRE) * i / M>{},
+                    std::integral_constant<int, PRE + (32 - PRE) * (i + 1) / M>{});
+        };
+        if constexpr (!has_acc) {
+          // No accumulation ahead of the scores: their first loads, then the
+          // first parts while they land.
+          static_for<0, 4>([&](auto cc) { load_init(sub + 1, cs[Q], cc); });
+          static_for<0, 3>([&](auto k) { load_row(sub + 1, 0, k); });
+          run_parts(std::integral_constant<int, 0>{}, std::integral_constant<int, PRE>{});
+          mask_init(sub + 1, cs[Q]);
         }
+        if constexpr (has_acc) {
+          const Chain<bf16>(&cp)[3] = ch[Q];
+          static_for<0, NSLICE>([&](auto slc) {
+            constexpr int sl = decltype(slc)::value;
+            constexpr int db = sl % NDB, s2 = sl / NDB;
+            // Slice sl + 2 of this sub-tile, else slice sl + 2 - NSLICE of the
+            // next accumulation (sub-tile sub), which follows in the next
+            // iteration or after the last one.
+            constexpr bool nxt = sl + 2 < NSLICE;
+            constexpr int lsub = nxt ? sub - 1 : sub, lsl = nxt ? sl + 2 : sl + 2 - NSLICE;
+            mfma_acc(ak[db], ta[sl & 1][0], cp[0].f[s2]);
+            load_tr(lsub, lsl, 0);
+            if constexpr (has_sc && sl == 0) load_init(sub + 1, cs[Q], 0);
+            if constexpr (has_sc && sl == 1) load_init(sub + 1, cs[Q], 2);
+            if constexpr (has_sc && sl == 2) load_row(sub + 1, 0, 0);
+            if constexpr (has_sc && sl == 3) load_row(sub + 1, 0, 2);
+            after(std::integral_constant<int, 3 * sl>{});
+            mfma_acc(av[db], ta[sl & 1][2], cp[2].f[s2]);
+            load_tr(lsub, lsl, 2);
+            if constexpr (has_sc && sl == 0) load_init(sub + 1, cs[Q], 1);
+            if constexpr (has_sc && sl == 1) load_init(sub + 1, cs[Q], 3);
+            if constexpr (has_sc && sl == 2) load_row(sub + 1, 0, 1);
+            after(std::integral_constant<int, 3 * sl + 1>{});
+            mfma_acc(ak[db], ta[sl & 1][1], cp[1].f[s2]);
+            load_tr(lsub, lsl, 1);
+            if constexpr (has_sc && sl == 3) mask_init(sub + 1, cs[Q]);
+            after(std::integral_constant<int, 3 * sl + 2>{});
+          });
+        }
+        if constexpr (has_sc) {
+          f32x16(&z)[4] = cs[Q];
+          static_for<0, NKS>([&](auto ksc) {
+            constexpr int ks = decltype(ksc)::value;
+            constexpr bool more = ks + 1 < NKS;
+            constexpr int i0 = NA + 5 * ks;
+            mfma_va(z[1], xr[1], kf[ks]);
+            if constexpr (more) load_row(sub + 1, ks + 1, 1);
+            after(std::integral_constant<int, i0>{});
+            mfma_va(z[0], xr[0], kf[ks]);
+            after(std::integral_constant<int, i0 + 1>{});
+            mfma_va(z[1], xr[0], ukf[ks]);
+            if constexpr (more) load_row(sub + 1, ks + 1, 0);
+            after(std::integral_constant<int, i0 + 2>{});
+            mfma_va(z[2], xr[2], vf[ks]);
+            after(std::integral_constant<int, i0 + 3>{});
+            mfma_va(z[3], xr[2], uvf[ks]);
+            if constexpr (more) load_row(sub + 1, ks + 1, 2);
+            after(std::integral_constant<int, i0 + 4>{});
+          });
+        }
+      };
+
+      // Tile head: scores of sub-tile 0 (nothing to overlap), with the first
+      // two slices of the first accumulation loaded behind them.
+      static_for<0, 4>([&](auto cc) { load_init(0, cs[0], cc); });
+      static_for<0, 3>([&](auto k) { load_row(0, 0, k); });
+      mask_init(0, cs[0]);
+      static_for<0, NKS>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        constexpr bool more = ks + 1 < NKS;
+        mfma_va(cs[0][1], xr[1], kf[ks]);
+        if constexpr (more) load_row(0, ks + 1, 1);
+        mfma_va(cs[0][0], xr[0], kf[ks]);
+        mfma_va(cs[0][1], xr[0], ukf[ks]);
+        if constexpr (more) load_row(0, ks + 1, 0);
+        mfma_va(cs[0][2], xr[2], vf[ks]);
+        mfma_va(cs[0][3], xr[2], uvf[ks]);
+        if constexpr (more) load_row(0, ks + 1, 2);
+      });
+      static_for<0, 2>([&](auto sl) { static_for<0, 3>([&](auto k) { load_tr(0, sl, k); }); });
+      static_for<0, NSUB>([&](auto subc) { iteration(subc); });
+      // Tail: accumulation of the last sub-tile (its first two slices are
+      // already loaded).
+      {
+        const Chain<bf16>(&cp)[3] = ch[(NSUB - 1) & 1];
+        static_for<0, NSLICE>([&](auto slc) {
+          constexpr int sl = decltype(slc)::value;
+          constexpr int db = sl % NDB, s2 = sl / NDB;
+          constexpr bool nxt = sl + 2 < NSLICE;
+          mfma_acc(ak[db], ta[sl & 1][0], cp[0].f[s2]);
+          if constexpr (nxt) load_tr(NSUB - 1, sl + 2, 0);
+          mfma_acc(av[db], ta[sl & 1][2], cp[2].f[s2]);
+          if constexpr (nxt) load_tr(NSUB - 1, sl + 2, 2);
+          mfma_acc(ak[db], ta[sl & 1][1], cp[1].f[s2]);
+          if constexpr (nxt) load_tr(NSUB - 1, sl + 2, 1);
+        });
       }
-      acc_w(NSUB - 1, ch[(NSUB - 1) & 1], [](int) {});
     };
 
     if constexpr (SPLIT) {
