@@ -132,7 +132,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   static_assert(NSTAGE * STAGE <= (int)kStageMask + 1, "stage region larger than its offset mask");
   __shared__ __attribute__((aligned(1024))) char stages[NSTAGE * STAGE];
   __shared__ __attribute__((aligned(1024))) char ops[2][4 * OPB];
-  __shared__ float rowx[2][4][32];  // alpha and E° handed from producer to consumer
+  __shared__ float rowx[4][32];  // alpha handed from producer to consumer
 
   const int nblk = (a.N + kResRows - 1) / kResRows;
   const int wid = xcd_remap(blockIdx.x, gridDim.x);
@@ -191,12 +191,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // D = rowsum(dO * O) of this row, computed here and written for the column pass.
     const float Di = resident_rowdot<D>(df, head_of<float>(a.o, bb, hd), row, N);
     const float nl2 = -Li * kLog2e;
-    // eob_p: E° summed from the bf16-rounded products P t0 that the matrix core
-    // accumulates into Omega.  gQ = tau (Omega - alpha R' - E° B) uses it, so the
-    // rounded operands cancel the way the exact ones do (Sum_j (P t0 - E° P) = 0;
-    // on a row whose P sits on one key those terms cancel exactly).  E and the
-    // column pass keep the unrounded E°.
-    float alpha_p = 0.0f, eo_p = 0.0f, eob_p = 0.0f;
+    float alpha_p = 0.0f, eo_p = 0.0f;
     rd.init();
     f32x16 S[2], F[2], DP[2], C[2];  // score chains, double buffered across slots
     const lds_p ob0 = (lds_p)ops[0] + wi * OPB + 16 * l;  // this wave's operand buffers
@@ -205,11 +200,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // A operand `which` (0 K, 1 V, 2 U_K, 3 U_V) of k-step ks of a key
-    // tile: rows of the stage at offset rel.
-    auto rd_a = [&](uint32_t rel, int ks, int which) {
-      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(stage_ptr(rel, rd.row[ks]) +
-                                                                                 which * W::BYTES);
+    // A operand `which` (0 K, 1 V, 2 U_K, 3 U_V) of a k-step whose rows start
+    // at b (one address per k-step; the tensors sit at constant offsets).
+    auto rd_a = [&](lds_cp b, int which) {
+      return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(b + which * W::BYTES);
     };
     // Scores of key tile t into set P: per k-step ks, S += K q, F += K u_q,
     // dP += V do, C += U_V do, F += U_K q; group(g) runs after MFMA g
@@ -218,7 +212,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto scores = [&](auto Pc, int t, auto&& group) {
       constexpr int P = decltype(Pc)::value;
       const uint32_t rel = stage_off(t);
-      bf16x8 xk = rd_a(rel, 0, 0), xv = rd_a(rel, 0, 1), xuk = rd_a(rel, 0, 2), xuv = rd_a(rel, 0, 3);
+      lds_cp bk = stage_ptr(rel, rd.row[0]);
+      bf16x8 xk = rd_a(bk, 0), xv = rd_a(bk, 1), xuk = rd_a(bk, 2), xuv = rd_a(bk, 3);
       sched_fence();
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -234,7 +229,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           sched_fence();
           mfma_vv(F[P], xk, uqf[ks]);
         }
-        if (more) xk = rd_a(rel, ks + 1, 0);
+        if (more) {
+          bk = stage_ptr(rel, rd.row[ks + 1]);
+          xk = rd_a(bk, 0);
+        }
         group(5 * ks + 1);
         sched_fence();
         if (ks == 0) {
@@ -242,7 +240,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
           mfma_vv(DP[P], xv, df[ks]);
         }
-        if (more) xv = rd_a(rel, ks + 1, 1);
+        if (more) xv = rd_a(bk, 1);
         group(5 * ks + 2);
         sched_fence();
         if (ks == 0) {
@@ -250,11 +248,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         } else {
           mfma_vv(C[P], xuv, df[ks]);
         }
-        if (more) xuv = rd_a(rel, ks + 1, 3);
+        if (more) xuv = rd_a(bk, 3);
         group(5 * ks + 3);
         sched_fence();
         mfma_vv(F[P], xuk, qf[ks]);
-        if (more) xuk = rd_a(rel, ks + 1, 2);
+        if (more) xuk = rd_a(bk, 2);
         group(5 * ks + 4);
         sched_fence();
       }
@@ -293,8 +291,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int w = idx >> 1;  // word w of each chain: k-half w / 4, word w % 4
         const uint32_t wp = pack_bf16(pair[0], p), wpf = pack_bf16(pair[1], pf), wpt = pack_bf16(pair[2], pt),
                        wds = pack_bf16(pair[3], ds);
-        add_here(eob_p, __builtin_bit_cast(float, wpt << 16));
-        add_here(eob_p, __builtin_bit_cast(float, wpt & 0xffff0000u));
         typedef __attribute__((address_space(3))) u32x4* wptr;
         const u32x4 words = {wp, wpf, wpt, wds};
         *reinterpret_cast<wptr>(obuf + op_off(w)) = words;
@@ -350,10 +346,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const float alpha = half_sum(alpha_p);
     const float eo = half_sum(eo_p);
-    const float eob = half_sum(eob_p);
     if (hh == 0) {
-      rowx[0][wi][l] = alpha;
-      rowx[1][wi][l] = eob;
+      rowx[wi][l] = alpha;
       if (row < N) {
         a.alpha[rv + row] = alpha;
         a.E[rv + row] = eo - alpha * Di;
@@ -377,6 +371,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const lds_cp ob0 = (lds_cp)ops[0] + wi * OPB + 16 * l;
     const lds_cp ob1 = (lds_cp)ops[1] + wi * OPB + 16 * l;
     rd.init();
+    float eob_c = 0.0f;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -409,6 +404,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           u32x4 grp[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) grp[j] = *reinterpret_cast<rp>(o + op_off(4 * s2 + j));
+          // E° from the bf16-rounded products P t0 that the matrix core
+          // accumulates into Omega: gQ = tau (Omega - alpha R' - E° B) uses
+          // it, so the rounded operands cancel the way the exact ones do
+          // (Sum_j (P t0 - E° P) = 0; on a row whose P sits on one key those
+          // terms cancel exactly).  E and the column pass keep the unrounded
+          // E°.  This lane holds 16 of the row's keys per tile; the other
+          // half of the wave holds the rest.
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            eob_c += __builtin_bit_cast(float, grp[j][2] << 16) + __builtin_bit_cast(float, grp[j][2] & 0xffff0000u);
           auto opnd = [&](int k) {
             const u32x4 v = {grp[0][k], grp[1][k], grp[2][k], grp[3][k]};
             return __builtin_bit_cast(bf16x8, v);
@@ -434,8 +439,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vfence4(ag[db], aom[db], ar[db], abk[db]);
     __syncthreads();  // alpha and E° of the producers are in LDS
-    const float alpha = rowx[0][wi][l & 31];
-    const float eob = rowx[1][wi][l & 31];
+    const float alpha = rowx[wi][l & 31];
+    const float eob = half_sum(eob_c);
     const HeadPtr<float> o = head_of<float>(a.o, bb, hd);
     float* gq = head_out(a.r0, bb, hd);
     float* gdo = head_out(a.r3, bb, hd);
