@@ -34,3 +34,14 @@ from .streaming import (  # noqa: F401
     row_pass,
     row_state,
 )
+from .dropout import (  # noqa: F401
+    backward_dropout,
+    bob_dropout,
+    bob_dropout_heads,
+    dropout_mask,
+    forward_dropout,
+    keep_bytes,
+    philox4x64_10,
+    phi_dropout,
+    threshold,
+)
