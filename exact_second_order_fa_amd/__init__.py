@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libfa.so")
 FA_OK = 0
 # fa_version() the binding needs: 1.1 added fa_problem.H_kv; an older library
 # would read key-side tensors with the query-head count.
-MIN_VERSION = 10100
+MIN_VERSION = 10200
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_STRIDE", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_UNSUPPORTED", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP",
@@ -47,7 +47,8 @@ class FaError(RuntimeError):
 class FaProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d", ctypes.c_int64), ("scale", ctypes.c_float), ("causal", ctypes.c_int32),
-                ("in_dtype", ctypes.c_int32), ("H_kv", ctypes.c_int64)]
+                ("in_dtype", ctypes.c_int32), ("H_kv", ctypes.c_int64), ("dropout", ctypes.c_float),
+                ("reserved", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 class FaTensor(ctypes.Structure):
@@ -113,10 +114,12 @@ def _torch():
     return torch
 
 
-def problem(B, H, N, d, in_dtype=FA_BF16, scale=None, causal=0, H_kv=0) -> FaProblem:
-    """H: query heads; H_kv: key/value heads (0 = H; otherwise a divisor of H)."""
+def problem(B, H, N, d, in_dtype=FA_BF16, scale=None, causal=0, H_kv=0, dropout=0.0, seed=0) -> FaProblem:
+    """H: query heads; H_kv: key/value heads (0 = H; otherwise a divisor of H);
+    dropout: rate p in [0, 1) with generator key ``seed`` (the same pair for
+    fa_fwd, fa_bwd and fa_bob)."""
     return FaProblem(int(B), int(H), int(N), int(d), float(-1.0 if scale is None else scale),
-                     int(causal), int(in_dtype), int(H_kv))
+                     int(causal), int(in_dtype), int(H_kv), float(dropout), 0, int(seed) & (2 ** 64 - 1))
 
 
 def tensor_arg(t) -> FaTensor:
@@ -179,13 +182,14 @@ def _call(name, status):
         raise FaError(status, name)
 
 
-def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, causal=False):
+def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, causal=False, dropout=0.0, seed=0):
     """Forward: returns (O fp32 [B,H,N,d], L fp32 [B,H,N], natural-log
     log-sum-exp of tau q.k over the (causally) valid keys).  k, v may have
-    fewer heads than q (grouped-query / multi-query attention)."""
+    fewer heads than q (grouped-query / multi-query attention).  With
+    ``dropout`` > 0, O = (P * g) V for the keep mask g of (dropout, seed)."""
     torch = _torch()
     B, H, N, d, Hkv = _check_inputs((q,), (k, v))
-    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
     o = _f32_like(q, o)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -214,11 +218,12 @@ def _workspace(nbytes, device, ws):
 
 
 def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None, stream=None,
-           causal=False):
+           causal=False, dropout=0.0, seed=0):
     """First backward: returns (dQ, dK, dV) fp32 and the workspace holding D.
-    dK, dV have k's heads (sums over each group's query heads)."""
+    dK, dV have k's heads (sums over each group's query heads).  ``dropout``
+    and ``seed`` must be the forward's."""
     B, H, N, d, Hkv = _check_inputs((q, dout), (k, v))
-    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
     dq, dk, dv = _f32_like(q, dq), _f32_like(k, dk), _f32_like(k, dv)
     nbytes = int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
     ws = _workspace(nbytes, q.device, ws)
@@ -231,16 +236,18 @@ def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None
 
 
 def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=None, gdo=None,
-           ws=None, stream=None, phase=None, causal=False, schedule=None):
+           ws=None, stream=None, phase=None, causal=False, schedule=None, dropout=0.0, seed=0):
     """Backward-over-backward: gradients of <dQ,U_Q> + <dK,U_K> + <dV,U_V> with
     respect to Q, K, V and dO (k, v, uk, uv and gK, gV may have fewer heads
     than q: grouped-query / multi-query attention).  Returns (gQ, gK, gV, gdO, ws) with
     ws = [D | alpha | E], each [B, H, N] fp32.  ``phase`` (0, 1 or 2) calls
     fa_bob_phase instead, launching only that kernel.  ``schedule`` (one of
     the SCHED_* constants) calls fa_bob_schedule: the schedule ablation of
-    the pages' appendix G.1 (phases 0-3 for the three-pass schedule)."""
+    the pages' appendix G.1 (phases 0-3 for the three-pass schedule).
+    ``dropout`` and ``seed`` must be the forward's (the pages' analytical
+    dropout extension)."""
     B, H, N, d, Hkv = _check_inputs((q, dout, uq), (k, v, uk, uv))
-    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
     gq, gdo = _f32_like(q, gq), _f32_like(q, gdo)
     gk, gv = _f32_like(k, gk), _f32_like(k, gv)
     lib = load_library()

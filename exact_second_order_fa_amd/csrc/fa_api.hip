@@ -15,7 +15,7 @@ using fa::Args;
 using fa::bf16;
 using fa::TDesc;
 
-constexpr int kVersion = 1 * 10000 + 1 * 100 + 0;  // 1.1: fa_problem.H_kv
+constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.1: fa_problem.H_kv; 1.2: dropout, seed
 
 struct Ctx {
   int64_t B, H, N, d;
@@ -24,6 +24,10 @@ struct Ctx {
   bool bf;
   bool causal;
   float tau, pow2, rho;
+  bool drop;            // dropout with a threshold > 0
+  uint32_t drop_thr;    // round(256 p)
+  float drop_scale;     // 256 / (256 - drop_thr)
+  uint64_t seed;
 };
 
 fa_status check_problem(const fa_problem* p, Ctx* c) {
@@ -50,6 +54,15 @@ fa_status check_problem(const fa_problem* p, Ctx* c) {
     tau = 1.0f / sqrtf((float)p->d);
   }
   if (!isfinite(tau)) return FA_ERR_UNSUPPORTED;
+  // Dropout rate p in [0, 1); the kernels keep an element with probability
+  // 1 - t / 256, t = round(256 p), which must stay below 256.
+  if (!(p->dropout >= 0.0f && p->dropout < 1.0f)) return FA_ERR_UNSUPPORTED;
+  const int thr = (int)floorf(p->dropout * 256.0f + 0.5f);
+  if (thr > 255) return FA_ERR_UNSUPPORTED;
+  c->drop = thr > 0;
+  c->drop_thr = (uint32_t)thr;
+  c->drop_scale = 256.0f / (float)(256 - thr);
+  c->seed = p->seed;
   int ex = 0;
   const float m = frexpf(tau, &ex);  // tau = m * 2^ex, m in [0.5, 1)
   c->B = p->B;
@@ -106,6 +119,9 @@ Args base_args(const Ctx& c) {
   a.pow2 = c.pow2;
   a.rho = c.rho;
   a.c1 = fa::kLog2e * c.rho;
+  a.seed = c.seed;
+  a.drop_thr = c.drop_thr;
+  a.drop_scale = c.drop_scale;
   return a;
 }
 
@@ -149,9 +165,14 @@ struct Tiles {
   static constexpr int TS = (sizeof(T) == 2 && D == 64) ? 64 : 32;
 };
 
+// Dropout runs on the portable kernels (register-staged tiles, one wave per
+// SIMD) for every input type; the tuned bf16 kernels carry no mask.
 template <typename T, int D, bool C>
 void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
-  if constexpr (sizeof(T) == 2)
+  if (c.drop)
+    hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
+                       st, a);
+  else if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
                        a);
   else
@@ -160,6 +181,16 @@ void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
 
 template <typename T, int D, bool C>
 void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
+  if (c.drop) {
+    Args b = a;
+    b.bs = nullptr;
+    launch_rowscalar<T, D>(c, b, st);
+    hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads),
+                       0, st, b);
+    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_cols(c)),
+                       dim3(fa::kThreads), 0, st, b);
+    return;
+  }
   if constexpr (sizeof(T) == 2) {
     // Row scalars D plus the staged chain inits (-L/rho, -D) of the column kernel.
     hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c, true)), dim3(256), 0, st, a);
@@ -188,6 +219,12 @@ template <typename T, int D, bool RHO1, bool C>
 void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int phase) {
   const dim3 g(grid_rows(c)), b(fa::kThreads), gc(grid_cols(c));
   auto want = [&](int ph) { return phase < 0 || phase == ph; };
+  if (c.drop) {  // two-pass schedule on the portable kernels (schedule 2 is refused earlier)
+    if (want(0)) launch_rowscalar<T, D>(c, a, st);
+    if (want(1)) hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), g, b, 0, st, a);
+    if (want(2)) hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), gc, b, 0, st, a);
+    return;
+  }
   // The bf16 two-pass row passes compute D themselves; phase 0 then launches nothing.
   if (want(0) && !(sizeof(T) == 2 && schedule != 2)) launch_rowscalar<T, D>(c, a, st);
   const int col_phase = schedule == 2 ? 3 : 2;
@@ -355,7 +392,7 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   Ctx c;
   FA_CHECK(check_problem(p, &c));
   if (schedule < 0 || schedule > 2) return FA_ERR_UNSUPPORTED;
-  if (schedule == 2 && !c.bf) return FA_ERR_UNSUPPORTED;
+  if (schedule == 2 && (!c.bf || c.drop)) return FA_ERR_UNSUPPORTED;
   if (phase < -1 || phase > (schedule == 2 ? 3 : 2)) return FA_ERR_UNSUPPORTED;
   FA_CHECK(check_tensor(c, q, c.esize));
   FA_CHECK(check_tensor(c, k, c.esize));

@@ -38,6 +38,9 @@ struct Args {
   int B, H, N;
   int Hk, G;                 // key/value heads and query heads per key/value head (H = Hk * G)
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
+  uint64_t seed;             // dropout: generator key
+  uint32_t drop_thr;         // dropout: keep an element iff its byte >= drop_thr (1..255)
+  float drop_scale;          // dropout: 256 / (256 - drop_thr), the kept elements' factor
 };
 
 template <typename T>
@@ -118,6 +121,69 @@ struct ScalarStager {
     }
   }
 };
+
+// ---------------------------------------------------------------------------
+// Dropout ([FlashBoB] appendix G, analytical dropout extension): the forward
+// multiplies P by a scaled keep mask g before the product with V, and the
+// first backward and the BoB take the same g.  Every pass recomputes g from a
+// counter-based generator instead of storing it: Philox4x64-10 (Salmon,
+// Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC
+// 2011), ten rounds that each take the 128-bit products of counter words 0
+// and 2 with two fixed odd multipliers, the key advancing by two Weyl
+// constants between rounds.  Element (i, j) of query head bh (= b H + h) uses
+// byte j % 8 of output word i % 4 of the block for counter (i / 4, j / 8, bh,
+// 0) and key (seed, 0); it is kept iff that byte is >= t = round(256 p), and
+// kept elements are scaled by 256 / (256 - t).
+struct U64x4 {
+  uint64_t w0, w1, w2, w3;
+};
+__device__ inline U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
+    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  return {c0, c1, c2, c3};
+}
+__device__ inline float keep_factor(const Args& a, uint64_t w, int byte) {
+  return ((uint32_t)(w >> (8 * byte)) & 0xffu) >= a.drop_thr ? a.drop_scale : 0.0f;
+}
+// g of the 16 elements a lane holds in a 32 x 32 sub-tile whose streamed
+// index starts at s0: row-side kernels (this lane's query row i, keys
+// s0 + acc_pos(idx)) and column-side kernels (this lane's key j, query rows
+// s0 + acc_pos(idx)).  Each group of four elements lies in one block.
+__device__ inline void drop_row16(const Args& a, int64_t bh, int i, int s0, float (&g)[16]) {
+  const int hh = lane_id() >> 5;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int j0 = s0 + acc_pos(4 * b, hh);
+    const U64x4 r = philox4x64_10((uint64_t)(i >> 2), (uint64_t)(j0 >> 3), (uint64_t)bh, 0, a.seed, 0);
+    const int wi = i & 3;
+    const uint64_t w = wi == 0 ? r.w0 : wi == 1 ? r.w1 : wi == 2 ? r.w2 : r.w3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[4 * b + e] = keep_factor(a, w, (j0 & 7) + e);
+  }
+}
+__device__ inline void drop_col16(const Args& a, int64_t bh, int s0, int j, float (&g)[16]) {
+  const int hh = lane_id() >> 5;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i0 = s0 + acc_pos(4 * b, hh);
+    const U64x4 r = philox4x64_10((uint64_t)(i0 >> 2), (uint64_t)(j >> 3), (uint64_t)bh, 0, a.seed, 0);
+    g[4 * b + 0] = keep_factor(a, r.w0, j & 7);
+    g[4 * b + 1] = keep_factor(a, r.w1, j & 7);
+    g[4 * b + 2] = keep_factor(a, r.w2, j & 7);
+    g[4 * b + 3] = keep_factor(a, r.w3, j & 7);
+  }
+}
 
 // Chain-initial value of a score-shaped accumulator from a staged per-row
 // scalar array: element idx gets sc[sub*32 + acc_pos(idx, hh)].
@@ -223,7 +289,7 @@ __global__ __launch_bounds__(256) void rowscalar_kernel(Args a) {
 // Forward ([FlashBoB] section 3; online softmax as in [FA2-triton]).
 // Resident: 32 query rows per wave.  Streamed: K (row copy, for S^T = K Q^T)
 // and V (transposed copy, for O^T += V^T P^T).  Running max in base-2 units.
-template <typename T, int D, int TS, bool CAUSAL>
+template <typename T, int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -289,7 +355,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       lsum = lsum * sc + ps;
       m = mn;
       Chain<T> cp;
-      cp.set(p);
+      if constexpr (DROP) {
+        // O = (P * g) V; the row sum (and L) is over P.
+        float g[16];
+        drop_row16(a, wk.bh, row, t * TS + sub * 32, g);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) g[idx] *= p[idx];
+        cp.set(g);
+      } else {
+        cp.set(p);
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -315,7 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // First backward, row side: dQ = tau dS K with dS = P (dP - D)
 // ([FlashBoB] section 3).  Resident: query rows.  Streamed: K, V.
-template <typename T, int D, int TS, bool CAUSAL>
+template <typename T, int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dq_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -366,11 +441,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
-      float ds[16];
+      float ds[16], g[16];
+      if constexpr (DROP) drop_row16(a, wk.bh, row, t * TS + sub * 32, g);
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
-        ds[idx] = p * (dp[idx] - Di);
+        // With dropout dP becomes g * (dO V^T).
+        ds[idx] = p * ((DROP ? g[idx] * dp[idx] : dp[idx]) - Di);
       }
       Chain<T> cds;
       cds.set(ds);
@@ -393,7 +470,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // First backward, column side: dV = P^T dO, dK = tau dS^T Q
 // ([FlashBoB] section 3).  Resident: key rows.  Streamed: Q, dO and the row
 // scalars (-L/rho, -D).
-template <typename T, int D, int TS, bool CAUSAL>
+template <typename T, int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -457,13 +534,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
-      const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
-      float p[16], ds[16];
+      // Without dropout dP starts from -D; with it dP = g * (dO V^T) - D.
+      const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, DROP ? zero16() : row_init<TS>(sc + TS, sub));
+      float p[16], ds[16], g[16];
+      f32x16 nd = zero16();
+      if constexpr (DROP) {
+        drop_col16(a, (int64_t)wk.b * a.H + wk.h + u / ntq, t * TS + sub * 32, col, g);
+        nd = row_init<TS>(sc + TS, sub);
+      }
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float pp = __builtin_amdgcn_exp2f(s[idx] * a.c1);
-        p[idx] = pp;
-        ds[idx] = pp * dp[idx];
+        p[idx] = DROP ? pp * g[idx] : pp;
+        ds[idx] = pp * (DROP ? fmaf(g[idx], dp[idx], nd[idx]) : dp[idx]);
       }
       Chain<T> cp, cds;
       cp.set(p);
@@ -507,7 +590,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Epilogue (the corrections of section 4.2, with R = R' + D Bk so that
 // alpha R + E Bk = alpha R' + E° Bk):
 //     E = E° - alpha D,  gdo = G - alpha o,  gq = tau (Om - alpha R' - E° Bk).
-template <typename T, int D, int TS, bool RHO1, bool CAUSAL>
+template <typename T, int D, int TS, bool RHO1, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -570,13 +653,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       f = mm_row<T, D, TS>(ukr, sub, qf, f);
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
       const f32x16 c = mm_row<T, D, TS>(uvr, sub, df, zero16());
-      float P[16], PF[16], PT[16], DS[16];
+      // Dropout (the analytical extension of [FlashBoB] appendix G): dP and
+      // C become g * (dO V^T) and g * (dO U_V^T); the products with V and
+      // U_V (the d~(dO) accumulator G) take P * g; alpha, E°, Om, R' and Bk
+      // keep P.
+      float P[16], PF[16], PT[16], DS[16], g[16];
+      if constexpr (DROP) drop_row16(a, wk.bh, row, t * TS + sub * 32, g);
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
         const float F = RHO1 ? f[idx] : f[idx] * a.rho;
-        const float dpd = dp[idx] - Di;
-        const float t0 = fmaf(F, dpd, c[idx]);
+        const float dpd = (DROP ? g[idx] * dp[idx] : dp[idx]) - Di;
+        const float t0 = fmaf(F, dpd, DROP ? g[idx] * c[idx] : c[idx]);
         P[idx] = p;
         PF[idx] = p * F;
         PT[idx] = p * t0;
@@ -584,11 +672,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         alpha_p += PF[idx];
         eo_p += PT[idx];
       }
-      Chain<T> cp, cpf, cpt, cds;
+      Chain<T> cp, cpf, cpt, cds, cpg, cpfg;
       cp.set(P);
       cpf.set(PF);
       cpt.set(PT);
       cds.set(DS);
+      if constexpr (DROP) {
+        float PG[16], PFG[16];
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          PG[idx] = P[idx] * g[idx];
+          PFG[idx] = PF[idx] * g[idx];
+        }
+        cpg.set(PG);
+        cpfg.set(PFG);
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -597,8 +695,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const typename E::frag xv = tr_frag<T, D, TS>(vt, db, sub, s2);
           const typename E::frag xk = tr_frag<T, D, TS>(kt, db, sub, s2);
           const typename E::frag xuk = tr_frag<T, D, TS>(ukt, db, sub, s2);
-          ag[db] = E::mma(xuv, cp.f[s2], ag[db]);
-          ag[db] = E::mma(xv, cpf.f[s2], ag[db]);
+          ag[db] = E::mma(xuv, DROP ? cpg.f[s2] : cp.f[s2], ag[db]);
+          ag[db] = E::mma(xv, DROP ? cpfg.f[s2] : cpf.f[s2], ag[db]);
           aom[db] = E::mma(xk, cpt.f[s2], aom[db]);
           aom[db] = E::mma(xuk, cds.f[s2], aom[db]);
           ar[db] = E::mma(xk, cds.f[s2], ar[db]);
@@ -650,7 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   P = exp(tau S - L),   d~P - E = C' + h dPD,
 //   d~S = P (d~P - E),    dS = P dPD,    W = P h,
 //   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
-template <typename T, int D, int TS, bool RHO1, bool CAUSAL>
+template <typename T, int D, int TS, bool RHO1, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_kernel(Args a) {
   typedef Elem<T> E;
   typedef Stage<T, D, TS> S;
@@ -724,8 +822,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
       f32x16 f = mm_row<T, D, TS>(uqr, sub, kf, row_init<TS>(sc + 2 * TS, sub));
       f = mm_row<T, D, TS>(qr, sub, ukf, f);
-      const f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, row_init<TS>(sc + TS, sub));
-      const f32x16 c = mm_row<T, D, TS>(dr, sub, uvf, row_init<TS>(sc + 3 * TS, sub));
+      // Dropout: dP = g * (dO V^T) - D and C' = g * (dO U_V^T) - alpha D - E,
+      // so the chains start at 0 and take the row scalars after g; W = P g h.
+      f32x16 dp = mm_row<T, D, TS>(dr, sub, vf, DROP ? zero16() : row_init<TS>(sc + TS, sub));
+      f32x16 c = mm_row<T, D, TS>(dr, sub, uvf, DROP ? zero16() : row_init<TS>(sc + 3 * TS, sub));
+      float g[16];
+      if constexpr (DROP) {
+        drop_col16(a, (int64_t)wk.b * a.H + wk.h + u / ntq, t * TS + sub * 32, col, g);
+        const f32x16 nd = row_init<TS>(sc + TS, sub), nc = row_init<TS>(sc + 3 * TS, sub);
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) {
+          dp[idx] = fmaf(g[idx], dp[idx], nd[idx]);
+          c[idx] = fmaf(g[idx], c[idx], nc[idx]);
+        }
+      }
       float DT[16], DS[16], W[16];
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
@@ -734,7 +844,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float x = fmaf(h, dp[idx], c[idx]);
         DT[idx] = p * x;
         DS[idx] = p * dp[idx];
-        W[idx] = p * h;
+        W[idx] = DROP ? p * g[idx] * h : p * h;
       }
       Chain<T> cdt, cds, cw;
       cdt.set(DT);

@@ -80,7 +80,31 @@ typedef struct fa_problem {
   int32_t causal;   /* 0: full attention; 1: causal (key j > query i masked) */
   int32_t in_dtype; /* an fa_dtype */
   int64_t H_kv;     /* key/value heads: 0 (= H) or a divisor of H */
+  float dropout;    /* dropout rate p in [0, 1); 0 = none (see below) */
+  int32_t reserved; /* set to 0 */
+  uint64_t seed;    /* dropout generator key */
 } fa_problem;
+
+/*
+ * Dropout ([FlashBoB] appendix G, "Analytical dropout extension"): the
+ * forward multiplies P by a scaled keep mask g before the product with V,
+ *   O = (P * g) V,   L unchanged (over P),
+ * the first backward uses dP = g * (dO V^T) and dV = (P * g)^T dO, and fa_bob
+ * returns the BoB of that first backward: the pages' identities with
+ * A = g * (dO V^T) in place of dP, C = g * (dO U_V^T), h = F - alpha, and
+ * P * g in the products with V and dO (d~(V) = (P g h)^T dO,
+ * d~(dO) = (P g) U_V + (P g h) V).
+ * g is not stored: every pass regenerates it from Philox4x64-10 (Salmon et
+ * al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011) with key
+ * (seed, 0).  Element (i, j) of query head bh = b * H + h takes byte j % 8
+ * of output word i % 4 of the block for counter (i / 4, j / 8, bh, 0); with
+ * t = round(256 p) (t <= 255, else FA_ERR_UNSUPPORTED) it is kept iff that
+ * byte is >= t, and kept elements are scaled by 256 / (256 - t).  p rounds
+ * to a multiple of 1/256; t = 0 means no dropout.  The same (p, seed) must be
+ * passed to fa_fwd, fa_bwd and fa_bob.  Dropout runs on the library's
+ * portable (register-staged) kernels, slower than the dropout-free bf16
+ * path; the three-pass schedule of fa_bob_schedule does not support it.
+ */
 
 typedef struct fa_tensor {
   void* ptr; /* device pointer */

@@ -40,15 +40,15 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 10100  # 1.1.0: fa_problem gained H_kv
+    assert lib.fa_version() == 10200  # 1.2.0: fa_problem gained dropout and seed (1.1.0: H_kv)
     for code in range(8):
         s = lib.fa_status_str(code).decode()
         assert s and s != "unknown status"
     assert lib.fa_status_str(99).decode() == "unknown status"
 
 
-def prob(B=1, H=2, N=100, d=64, scale=-1.0, causal=0, dt=fa.FA_BF16, Hkv=0):
-    return FaProblem(B, H, N, d, scale, causal, dt, Hkv)
+def prob(B=1, H=2, N=100, d=64, scale=-1.0, causal=0, dt=fa.FA_BF16, Hkv=0, dropout=0.0, seed=0):
+    return FaProblem(B, H, N, d, scale, causal, dt, Hkv, dropout, 0, seed)
 
 
 def test_problem_struct_layout(tmp_path):
@@ -62,14 +62,15 @@ def test_problem_struct_layout(tmp_path):
         pytest.skip("no C compiler")
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "fa.h"\n'
-                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(fa_problem), '
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(fa_problem), '
                    'offsetof(fa_problem, scale), offsetof(fa_problem, in_dtype), offsetof(fa_problem, H_kv), '
+                   'offsetof(fa_problem, dropout), offsetof(fa_problem, seed), '
                    'sizeof(fa_tensor)); return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.run([cc, "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
     assert got == [ctypes.sizeof(FaProblem), FaProblem.scale.offset, FaProblem.in_dtype.offset,
-                   FaProblem.H_kv.offset, ctypes.sizeof(FaTensor)]
+                   FaProblem.H_kv.offset, FaProblem.dropout.offset, FaProblem.seed.offset, ctypes.sizeof(FaTensor)]
 
 
 def test_workspace_sizes(lib):
@@ -114,6 +115,10 @@ def bob(lib, p, tensors=None, lse=FAKE, ws=FAKE, ws_bytes=1 << 30):
     (prob(H=2, Hkv=3), 2),   # more key/value heads than query heads
     (prob(H=4, Hkv=3), 2),   # not a divisor
     (prob(H=2, Hkv=-1), 2),
+    (prob(dropout=-0.1), 5),
+    (prob(dropout=1.0), 5),
+    (prob(dropout=0.999), 5),  # rounds to 256/256: nothing kept
+    (prob(dropout=float("nan")), 5),
 ])
 def test_problem_validation(lib, p, status):
     assert bob(lib, p) == status
@@ -195,6 +200,12 @@ def sched(lib, p, schedule, phase, ts=None):
 ])
 def test_schedule_validation(lib, schedule, phase, dt):
     assert sched(lib, prob(dt=dt), schedule, phase) == 5
+
+
+def test_three_pass_refuses_dropout(lib):
+    assert sched(lib, prob(dropout=0.1), 2, -1) == 5
+    # a rate that rounds to a zero threshold is no dropout
+    assert sched(lib, prob(dropout=0.001), 2, -1, [t(ptr=0)] + [t() for _ in range(11)]) == 1
 
 
 def test_schedule_checks_tensors_too(lib):

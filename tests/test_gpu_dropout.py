@@ -1,0 +1,77 @@
+"""Parity of the dropout path (fa_fwd, fa_bwd, fa_bob with a dropout rate and
+seed, through the C ABI) with the float64 dropout oracle, which draws the same
+Philox4x64-10 mask from its own implementation.  Every output is compared
+element by element, with the bars of the dropout-free tests (bf16 2e-2, fp32
+1e-4 relative to the oracle's maximum)."""
+import numpy as np
+import pytest
+
+from fa_inputs import make_inputs
+from oracle import bob_dropout_heads
+from tests.gpu_helpers import host, rel, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
+ALL = ("O", "L", "dQ", "dK", "dV", "D", "alpha", "E", "gQ", "gK", "gV", "gdO")
+
+
+def run_dropout(t, p, seed, causal):
+    import torch
+
+    import exact_second_order_fa_amd as fa
+
+    kw = dict(causal=causal, dropout=p, seed=seed)
+    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], **kw)
+    dq, dk, dv, _ = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], **kw)
+    gq, gk, gv, gdo, ws = fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"], **kw)
+    B, H, N, _ = t["q"].shape
+    D, alpha, E = fa.split_workspace(ws, B, H, N)
+    torch.cuda.synchronize()
+    return dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv, D=D, alpha=alpha, E=E, gQ=gq, gK=gk, gV=gv, gdO=gdo)
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d,dtype,p,causal", [
+    (1, 2, 2, 100, 64, "fp32", 0.1, False),   # ragged tile
+    (1, 1, 1, 128, 64, "fp32", 0.5, True),
+    (1, 2, 2, 130, 64, "bf16", 0.25, False),  # ragged resident block
+    (2, 2, 2, 97, 64, "bf16", 0.5, True),
+    (1, 4, 2, 64, 64, "bf16", 0.1, False),    # grouped-query heads
+    (1, 2, 2, 75, 128, "bf16", 0.2, False),   # d = 128
+    (1, 1, 1, 33, 128, "bf16", 0.9, True),
+])
+def test_dropout_parity(B, H, Hkv, N, d, dtype, p, causal):
+    seed = 1000 + N + d
+    say(f"dropout case B={B} H={H} H_kv={Hkv} N={N} d={d} {dtype} p={p} causal={causal} seed={seed}")
+    raw, f64 = make_inputs(B, H, N, d, seed, dtype, H_kv=Hkv)
+    got = run_dropout(to_device(raw, dtype), p, seed, causal)
+    ref = bob_dropout_heads(*(f64[n] for n in ("q", "k", "v", "do", "uq", "uk", "uv")), 1.0 / np.sqrt(d), p, seed,
+                            causal)
+    errs = {k: rel(host(got[k]), ref[k]) for k in ALL}
+    say("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, bad
+
+
+def test_dropout_rate_rounding_to_zero_is_the_dropout_free_path():
+    """A rate below 1/512 rounds to threshold 0: no element is dropped and the
+    library takes its dropout-free kernels (bit-identical outputs)."""
+    raw, _ = make_inputs(1, 2, 96, 64, 77, "bf16")
+    t = to_device(raw, "bf16")
+    a = run_dropout(t, 0.0, 5, False)
+    b = run_dropout(t, 0.001, 5, False)
+    for k in ALL:
+        assert np.array_equal(host(a[k]), host(b[k])), k
+
+
+def test_dropout_seed_determinism():
+    """The same (p, seed) reproduces every output bit for bit; another seed
+    draws another mask."""
+    raw, _ = make_inputs(1, 1, 64, 64, 78, "fp32")
+    t = to_device(raw, "fp32")
+    a = run_dropout(t, 0.3, 11, False)
+    b = run_dropout(t, 0.3, 11, False)
+    c = run_dropout(t, 0.3, 12, False)
+    for k in ALL:
+        assert np.array_equal(host(a[k]), host(b[k])), k
+    assert not np.array_equal(host(a["O"]), host(c["O"]))
