@@ -82,16 +82,17 @@ def device_inputs(w):
 class Runner:
     """Inputs, saved forward state and preallocated outputs of one workload."""
 
-    def __init__(self, w):
+    def __init__(self, w, dropout=0.0, seed=0):
         import torch
 
         import exact_second_order_fa_amd as fa
 
         self.fa, self.w = fa, w
+        self.drop = dict(dropout=dropout, seed=seed)
         self.t = device_inputs(w)
         shape = (w.B, w.H, w.N, w.d)
         kshape = (w.B, w.Hkv, w.N, w.d)  # key-side outputs: one per key/value head
-        self.o, self.lse = fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], causal=w.causal)
+        self.o, self.lse = fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], causal=w.causal, **self.drop)
         self.outs = [torch.empty(s, dtype=torch.float32, device="cuda") for s in (shape, kshape, kshape, shape)]
         code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP32
         self.ws = torch.empty(fa.bob_workspace_bytes(*shape, code, w.causal) // 4, dtype=torch.float32,
@@ -102,17 +103,18 @@ class Runner:
         t, g = self.t, self.outs
         self.fa.fa_bob(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], t["uq"], t["uk"], t["uv"],
                        gq=g[0], gk=g[1], gv=g[2], gdo=g[3], ws=self.ws, phase=phase, causal=self.w.causal,
-                       schedule=schedule)
+                       schedule=schedule, **self.drop)
 
     def fwd(self):
-        self.fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], o=self.o, lse=self.lse, causal=self.w.causal)
+        self.fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], o=self.o, lse=self.lse, causal=self.w.causal,
+                       **self.drop)
 
     def bwd(self):
         t, g = self.t, self.outs
         if not hasattr(self, "bws"):
             self.bws = None
         _, _, _, self.bws = self.fa.fa_bwd(t["q"], t["k"], t["v"], self.o, self.lse, t["do"], dq=g[0], dk=g[1],
-                                           dv=g[2], ws=self.bws, causal=self.w.causal)
+                                           dv=g[2], ws=self.bws, causal=self.w.causal, **self.drop)
 
 
 def time_steps(r, steps, warmup):
@@ -285,6 +287,8 @@ def main():
                     help="workloads of the three-pass vs two-pass schedule ablation ('' for none)")
     ap.add_argument("--only-ablation", action="store_true", help="run only the schedule ablation (profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--dropout", type=float, default=0.1,
+                    help="rate of the dropout-variant timing leg on the main workload (0: skip)")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU oracle sample (0: all)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (three times), the reference kernel "
@@ -352,6 +356,17 @@ def main():
         if name in PAGES_MS:
             sweep[name]["pages_ms_context"] = PAGES_MS[name]
 
+    # The dropout variant ([FlashBoB] appendix G) on the same workload: the
+    # portable kernels with the Philox mask, reported beside the headline.
+    dropout_leg = None
+    if args.dropout > 0:
+        del r
+        torch.cuda.empty_cache()
+        r = Runner(w, dropout=args.dropout, seed=1234)
+        d_ms = time_plain(r.bob, reps_for(settle(r.bob)))
+        dropout_leg = {"p": args.dropout, "workload": w.name, "fa_bob_ms": round(d_ms, 4),
+                       "tflops": round(w.bob_flops / (d_ms * 1e9), 1), "kernels": "portable, mask from Philox4x64-10"}
+
     line = {
         "metric": "fa_bob TFLOP/s (38 B H N^2 d flops per call) and fraction of bf16 dense MFMA peak",
         "value": round(value, 2),
@@ -376,6 +391,7 @@ def main():
                        "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)},
         "prerequisites": prereq,
         "sweep": sweep,
+        "dropout_variant": dropout_leg,
     }
     if abl_names:
         del r

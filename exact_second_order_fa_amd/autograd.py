@@ -24,6 +24,9 @@ library takes dO and the cotangents in the input dtype, so for bf16 inputs
 they are rounded to bf16 on the way in (as any bf16 attention kernel does);
 outputs are fp32 and autograd casts input gradients to the inputs' dtype.
 K and V may have fewer heads than Q (grouped-query / multi-query attention).
+With a dropout rate, every call passes the same (rate, seed), so the forward,
+the first backward and the BoB see one mask (the pages' analytical dropout
+extension, appendix G).
 """
 from __future__ import annotations
 
@@ -49,10 +52,10 @@ class _NoThirdOrder(torch.autograd.Function):
 
 class _Attn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, scale, causal):
-        o, lse = fa_fwd(q, k, v, scale=scale, causal=causal)
+    def forward(ctx, q, k, v, scale, causal, dropout, seed):
+        o, lse = fa_fwd(q, k, v, scale=scale, causal=causal, dropout=dropout, seed=seed)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.scale, ctx.causal = scale, causal
+        ctx.scale, ctx.causal, ctx.drop = scale, causal, (dropout, seed)
         ctx.mark_non_differentiable(lse)
         # An absent gradient stays None (no zero-filled dO): _AttnBwd returns
         # none for O, and the first backward must not run again for nothing.
@@ -62,25 +65,26 @@ class _Attn(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do, _dlse):
         if do is None:
-            return None, None, None, None, None
+            return (None,) * 7
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = _AttnBwd.apply(q, k, v, o, lse, do.to(q.dtype), ctx.scale, ctx.causal)
-        return dq, dk, dv, None, None
+        dq, dk, dv = _AttnBwd.apply(q, k, v, o, lse, do.to(q.dtype), ctx.scale, ctx.causal, *ctx.drop)
+        return dq, dk, dv, None, None, None, None
 
 
 class _AttnBwd(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, o, lse, do, scale, causal):
-        dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, do.contiguous(), scale=scale, causal=causal)
+    def forward(ctx, q, k, v, o, lse, do, scale, causal, dropout, seed):
+        dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, do.contiguous(), scale=scale, causal=causal, dropout=dropout,
+                               seed=seed)
         ctx.save_for_backward(q, k, v, o, lse, do)
-        ctx.scale, ctx.causal = scale, causal
+        ctx.scale, ctx.causal, ctx.drop = scale, causal, (dropout, seed)
         ctx.set_materialize_grads(False)
         return dq, dk, dv
 
     @staticmethod
     def backward(ctx, uq, uk, uv):
         if uq is None and uk is None and uv is None:
-            return (None,) * 8
+            return (None,) * 10
         q, k, v, o, lse, do = ctx.saved_tensors
         dt = q.dtype
 
@@ -89,23 +93,24 @@ class _AttnBwd(torch.autograd.Function):
 
         with torch.no_grad():
             out = fa_bob(q, k, v, o, lse, do.contiguous(), cot(uq, q), cot(uk, k), cot(uv, v),
-                         scale=ctx.scale, causal=ctx.causal)[:4]
+                         scale=ctx.scale, causal=ctx.causal, dropout=ctx.drop[0], seed=ctx.drop[1])[:4]
         deps = [t for t in (q, k, v, do, uq, uk, uv) if t is not None and t.requires_grad]
         if torch.is_grad_enabled() and deps:
             # The caller asked for a graph of these gradients (create_graph):
             # make any further differentiation fail loudly.
             out = [_NoThirdOrder.apply(x, *deps) for x in out]
         gq, gk, gv, gdo = out
-        return gq, gk, gv, None, None, gdo, None, None
+        return gq, gk, gv, None, None, gdo, None, None, None, None
 
 
-def sdpa_bob(q, k, v, scale=None, causal=False):
+def sdpa_bob(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0):
     """O = softmax(scale q k^T [+ causal mask]) v for [B, H, N, d] tensors
     (bf16 or fp32; k, v with H or a divisor of H heads), differentiable twice
     through the library's kernels.  Returns O in fp32.  ``scale`` defaults to
-    1/sqrt(d)."""
+    1/sqrt(d).  ``dropout_p`` > 0 applies the library's dropout mask for
+    ``seed`` (O = (P * g) V); the same mask is used by both derivatives."""
     for t in (q, k, v):
         if t.dim() != 4 or t.stride(-1) != 1:
             raise ValueError("q, k, v must be [B, H, N, d] with a contiguous head dimension")
-    o, _ = _Attn.apply(q, k, v, scale, bool(causal))
+    o, _ = _Attn.apply(q, k, v, scale, bool(causal), float(dropout_p), int(seed))
     return o

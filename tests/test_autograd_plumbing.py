@@ -13,20 +13,24 @@ import torch
 import exact_second_order_fa_amd.autograd as ag
 
 calls = []
+drops = []  # (call, dropout, seed)
 
 
-def fa_fwd(q, k, v, scale=None, causal=False):
+def fa_fwd(q, k, v, scale=None, causal=False, dropout=0.0, seed=0):
     calls.append(("fwd", q.dtype, causal))
+    drops.append(("fwd", dropout, seed))
     return (q.float() * 2 + k.float() * 3 + v.float() * 5), q.float().sum(-1)
 
 
-def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False):
+def fa_bwd(q, k, v, o, lse, do, scale=None, causal=False, dropout=0.0, seed=0):
     calls.append(("bwd", do.dtype, causal))
+    drops.append(("bwd", dropout, seed))
     return do.float() * 7, do.float() * 11, do.float() * 13, None
 
 
-def fa_bob(q, k, v, o, lse, do, uq, uk, uv, scale=None, causal=False):
+def fa_bob(q, k, v, o, lse, do, uq, uk, uv, scale=None, causal=False, dropout=0.0, seed=0):
     calls.append(("bob", uq.dtype, uk.dtype, causal))
+    drops.append(("bob", dropout, seed))
     return uq.float() * 17, uk.float() * 19, uv.float() * 23, uq.float() * 29 + uv.float() * 31, None
 
 
@@ -36,6 +40,7 @@ def standins(monkeypatch):
     monkeypatch.setattr(ag, "fa_bwd", fa_bwd)
     monkeypatch.setattr(ag, "fa_bob", fa_bob)
     calls.clear()
+    drops.clear()
 
 
 def leaves(dtype=torch.float32, Hkv=2):
@@ -96,3 +101,14 @@ def test_rejects_non_contiguous_head_dim():
     q, k, v = leaves()
     with pytest.raises(ValueError):
         ag.sdpa_bob(q.transpose(2, 3), k, v)
+
+
+def test_dropout_rate_and_seed_reach_every_call():
+    """One mask for the forward, the first backward and the BoB: all three
+    calls get the same (rate, seed)."""
+    q, k, v = leaves()
+    o = ag.sdpa_bob(q, k, v, dropout_p=0.25, seed=2 ** 40 + 3)
+    g = torch.autograd.grad(0.5 * (o * o).sum(), (q, k, v), create_graph=True)
+    torch.autograd.grad(sum(x.sum() for x in g), (q, k, v))
+    assert [d[0] for d in drops] == ["fwd", "bwd", "bob", "bwd"]
+    assert all(d[1:] == (0.25, 2 ** 40 + 3) for d in drops)

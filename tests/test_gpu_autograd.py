@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import make_inputs
-from oracle import backward_dense, bob_dense, bob_dense_gqa, forward_dense
+from oracle import backward_dense, bob_dense, bob_dense_gqa, bob_dropout, dropout_mask, forward_dense
 from tests.gpu_helpers import host, rel, say
 
 pytestmark = pytest.mark.gpu
@@ -43,12 +43,12 @@ def tensors(raw, dtype, names, grad):
     return out
 
 
-def hvp(q, k, v, loss, z, causal):
+def hvp(q, k, v, loss, z, causal, dropout_p=0.0, seed=0):
     import torch
 
     from exact_second_order_fa_amd.autograd import sdpa_bob
 
-    o = sdpa_bob(q, k, v, causal=causal)
+    o = sdpa_bob(q, k, v, causal=causal, dropout_p=dropout_p, seed=seed)
     g = torch.autograd.grad(loss(o), (q, k, v), create_graph=True)
     s = sum((gi.float() * zi).sum() for gi, zi in zip(g, z))
     h = torch.autograd.grad(s, (q, k, v))
@@ -75,6 +75,29 @@ def test_hvp_linear_loss(dtype, causal):
                 errs["H z " + key[1]] = rel(host(h[i][b, hh]), ref[key])
             say("  " + " ".join(f"{k_}={v_:.1e}" for k_, v_ in errs.items()))
             assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype,causal", [("fp32", False), ("bf16", True)])
+def test_hvp_linear_loss_with_dropout(dtype, causal):
+    """With dropout the HVP of L = <O, W> is the BoB of the dropout backward
+    (oracle ``bob_dropout`` with the same Philox mask)."""
+    B, H, N, d, p, seed = 1, 2, 100, 64, 0.2, 4242
+    say(f"hvp linear loss with dropout {dtype} causal={causal}")
+    raw, f64 = make_inputs(B, H, N, d, 1130 + causal, dtype)
+    q, k, v = tensors(raw, dtype, ("q", "k", "v"), True)
+    W, zq, zk, zv = (t.float() for t in tensors(raw, dtype, ("do", "uq", "uk", "uv"), False))
+    o, g, h = hvp(q, k, v, lambda o: (o * W).sum(), (zq, zk, zv), causal, dropout_p=p, seed=seed)
+    tau = 1 / np.sqrt(d)
+    for hh in range(H):
+        gm = dropout_mask(hh, N, p, seed)
+        ref = bob_dropout(*(f64[n][0, hh] for n in ("q", "k", "v", "do", "uq", "uk", "uv")), tau, gm, causal=causal)
+        errs = {"O": rel(host(o[0, hh]), ref["O"])}
+        for i, key in enumerate(("dQ", "dK", "dV")):
+            errs[key] = rel(host(g[i][0, hh]), ref[key])
+        for i, key in enumerate(("gQ", "gK", "gV")):
+            errs["H z " + key[1]] = rel(host(h[i][0, hh]), ref[key])
+        say("  " + " ".join(f"{k_}={v_:.1e}" for k_, v_ in errs.items()))
+        assert max(errs.values()) <= TOL[dtype], errs
 
 
 @pytest.mark.parametrize("causal", [False, True])
