@@ -153,37 +153,114 @@ __device__ inline U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uin
   }
   return {c0, c1, c2, c3};
 }
-__device__ inline float keep_factor(const Args& a, uint64_t w, int byte) {
-  return ((uint32_t)(w >> (8 * byte)) & 0xffu) >= a.drop_thr ? a.drop_scale : 0.0f;
+__device__ inline float keep_byte(const Args& a, uint32_t w, int byte) {
+  return ((w >> (8 * byte)) & 0xffu) >= a.drop_thr ? a.drop_scale : 0.0f;
 }
-// g of the 16 elements a lane holds in a 32 x 32 sub-tile whose streamed
-// index starts at s0: row-side kernels (this lane's query row i, keys
-// s0 + acc_pos(idx)) and column-side kernels (this lane's key j, query rows
-// s0 + acc_pos(idx)).  Each group of four elements lies in one block.
-__device__ inline void drop_row16(const Args& a, int64_t bh, int i, int s0, float (&g)[16]) {
-  const int hh = lane_id() >> 5;
+
+// The wave shares the generator's work.  A 32 x 32 sub-tile covers 32 blocks
+// (8 groups of four query rows x 4 groups of eight keys); a row-side lane's 16
+// elements lie in two of them, which the other three rows of its group of
+// four use too, and a column-side lane's in four, which the other seven keys
+// of its group of eight use too.  So instead of each lane running every block
+// it touches, each lane runs ONE block per granule of NS sub-tiles (NS = 2:
+// every block of the granule exactly once; NS = 1: each block by two lanes)
+// and the words move to the lanes that use them by lane exchanges inside
+// groups of M lanes (xor_transpose): 4-8x fewer generator calls.
+
+// Lanes g = lane % M of a group each hold items A[q] (K dwords each), q =
+// 0..M-1, of their own block; afterwards lane g holds in A[s] item g of lane
+// s's block.  One stage per lane bit: a lane keeps the items whose index has
+// that bit equal to its own, swaps the others with the lane that differs in
+// that bit, and re-slots both by the bit of the lane they came from.
+template <int M, int K>
+__device__ inline void xor_transpose(uint32_t (&A)[M][K]) {
+  const int g = lane_id() & (M - 1);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int j0 = s0 + acc_pos(4 * b, hh);
-    const U64x4 r = philox4x64_10((uint64_t)(i >> 2), (uint64_t)(j0 >> 3), (uint64_t)bh, 0, a.seed, 0);
-    const int wi = i & 3;
-    const uint64_t w = wi == 0 ? r.w0 : wi == 1 ? r.w1 : wi == 2 ? r.w2 : r.w3;
+  for (int bit = 1; bit < M; bit <<= 1) {
+    const bool up = (g & bit) != 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) g[4 * b + e] = keep_factor(a, w, (j0 & 7) + e);
+    for (int s = 0; s < M; ++s) {
+      if (s & bit) continue;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const uint32_t send = up ? A[s][k] : A[s | bit][k];
+        const uint32_t recv = (uint32_t)__shfl_xor((int)send, bit);
+        A[s][k] = up ? recv : A[s][k];
+        A[s | bit][k] = up ? A[s | bit][k] : recv;
+      }
+    }
   }
 }
-__device__ inline void drop_col16(const Args& a, int64_t bh, int s0, int j, float (&g)[16]) {
-  const int hh = lane_id() >> 5;
+
+// Row side: this lane's query row i (i % 4 = lane % 4) and NS sub-tiles of 32
+// keys from s0 (a multiple of 32).  Element idx of sub-tile sub sits at key
+// s0 + 32 sub + 16 (b / 2) + 8 hh + 4 (b % 2) + e (b = idx / 4, e = idx % 4):
+// block (i / 4, s0 / 8 + 4 sub + 2 (b / 2) + hh), word i % 4, byte 4 (b % 2)
+// + e.  Lane r = i % 4 of the quad runs the block of sub = r / 2 (NS = 2),
+// b / 2 = r % 2; the quad then swaps words so that lane r holds word r of
+// all four.
+template <int NS>
+struct DropRow {
+  static_assert(NS == 1 || NS == 2, "granule of one or two sub-tiles");
+  uint32_t w[4][2];  // [lane of the quad that ran the block][low / high dword of word i % 4]
+  __device__ inline void init(const Args& a, int64_t bh, int i, int s0) {
+    const int hh = lane_id() >> 5, r = lane_id() & 3;
+    const int sub = NS == 2 ? r >> 1 : 0;
+    const U64x4 x = philox4x64_10((uint64_t)(i >> 2), (uint64_t)(s0 / 8 + 4 * sub + 2 * (r & 1) + hh), (uint64_t)bh,
+                                  0, a.seed, 0);
+    const uint64_t ww[4] = {x.w0, x.w1, x.w2, x.w3};
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int i0 = s0 + acc_pos(4 * b, hh);
-    const U64x4 r = philox4x64_10((uint64_t)(i0 >> 2), (uint64_t)(j >> 3), (uint64_t)bh, 0, a.seed, 0);
-    g[4 * b + 0] = keep_factor(a, r.w0, j & 7);
-    g[4 * b + 1] = keep_factor(a, r.w1, j & 7);
-    g[4 * b + 2] = keep_factor(a, r.w2, j & 7);
-    g[4 * b + 3] = keep_factor(a, r.w3, j & 7);
+    for (int q = 0; q < 4; ++q) {
+      w[q][0] = (uint32_t)ww[q];
+      w[q][1] = (uint32_t)(ww[q] >> 32);
+    }
+    xor_transpose<4, 2>(w);
   }
-}
+  __device__ inline void get(const Args& a, int sub, float (&g)[16]) const {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t d = w[(NS == 2 ? 2 * sub : 0) + (b >> 1)][b & 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[4 * b + e] = keep_byte(a, d, e);
+    }
+  }
+};
+
+// Column side: this lane's key j (j % 8 = lane % 8) and NS sub-tiles of 32
+// query rows from s0 (a multiple of 32).  Element idx of sub-tile sub sits at
+// row s0 + 32 sub + 16 (b / 2) + 8 hh + 4 (b % 2) + e: block (s0 / 4 + 8 sub
+// + 4 (b / 2) + 2 hh + b % 2, j / 8), word e, byte j % 8.  Lane r = j % 8 of
+// the group of eight runs the block of sub = r / 4 (NS = 2), b = r % 4,
+// packs byte q of its four words into item q, and the group swaps items so
+// that lane r holds item r of all eight blocks.
+template <int NS>
+struct DropCol {
+  static_assert(NS == 1 || NS == 2, "granule of one or two sub-tiles");
+  uint32_t w[8][1];  // [lane of the group that ran the block]: byte e = word e's byte j % 8
+  __device__ inline void init(const Args& a, int64_t bh, int s0, int j) {
+    const int hh = lane_id() >> 5, r = lane_id() & 7;
+    const int sub = NS == 2 ? r >> 2 : 0, b = r & 3;
+    const U64x4 x = philox4x64_10((uint64_t)(s0 / 4 + 8 * sub + 4 * (b >> 1) + 2 * hh + (b & 1)),
+                                  (uint64_t)(j >> 3), (uint64_t)bh, 0, a.seed, 0);
+    const uint64_t ww[4] = {x.w0, x.w1, x.w2, x.w3};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t item = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) item |= (uint32_t)((ww[e] >> (8 * q)) & 0xffu) << (8 * e);
+      w[q][0] = item;
+    }
+    xor_transpose<8, 1>(w);
+  }
+  __device__ inline void get(const Args& a, int sub, float (&g)[16]) const {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t d = w[(NS == 2 ? 4 * sub : 0) + b][0];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[4 * b + e] = keep_byte(a, d, e);
+    }
+  }
+};
 
 // Chain-initial value of a score-shaped accumulator from a staged per-row
 // scalar array: element idx gets sc[sub*32 + acc_pos(idx, hh)].
@@ -331,6 +408,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float* kb = kbias[t & 1];
     const T* kr = lds[t & 1];
     const T* vt = lds[t & 1] + S::ELEMS + S::ROW_ELEMS;
+    DropRow<NSUB> dm;
+    if constexpr (DROP) dm.init(a, wk.bh, row, t * TS);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
@@ -358,7 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if constexpr (DROP) {
         // O = (P * g) V; the row sum (and L) is over P.
         float g[16];
-        drop_row16(a, wk.bh, row, t * TS + sub * 32, g);
+        dm.get(a, sub, g);
 #pragma unroll
         for (int idx = 0; idx < 16; ++idx) g[idx] *= p[idx];
         cp.set(g);
@@ -437,12 +516,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* kr = lds[t & 1];
     const T* kt = kr + S::ROW_ELEMS;
     const T* vr = kr + S::ELEMS;
+    DropRow<NSUB> dm;
+    if constexpr (DROP) dm.init(a, wk.bh, row, t * TS);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
       const f32x16 dp = mm_row<T, D, TS>(vr, sub, df, zero16());
       float ds[16], g[16];
-      if constexpr (DROP) drop_row16(a, wk.bh, row, t * TS + sub * 32, g);
+      if constexpr (DROP) dm.get(a, sub, g);
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
@@ -531,6 +612,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* dr = qr + S::ELEMS;
     const T* dt = dr + S::ROW_ELEMS;
     const float* sc = scl[u & 1];
+    DropCol<NSUB> dm;
+    if constexpr (DROP) dm.init(a, (int64_t)wk.b * a.H + wk.h + u / ntq, t * TS, col);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
@@ -539,7 +622,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       float p[16], ds[16], g[16];
       f32x16 nd = zero16();
       if constexpr (DROP) {
-        drop_col16(a, (int64_t)wk.b * a.H + wk.h + u / ntq, t * TS + sub * 32, col, g);
+        dm.get(a, sub, g);
         nd = row_init<TS>(sc + TS, sub);
       }
 #pragma unroll
@@ -646,6 +729,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* ukt = ukr + S::ROW_ELEMS;
     const T* uvr = kr + 3 * S::ELEMS;
     const T* uvt = uvr + S::ROW_ELEMS;
+    DropRow<NSUB> dm;
+    if constexpr (DROP) dm.init(a, wk.bh, row, t * TS);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(kr, sub, qf, key_init<TS, CAUSAL>(kb, sub, t * TS, row));
@@ -658,7 +743,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // U_V (the d~(dO) accumulator G) take P * g; alpha, E°, Om, R' and Bk
       // keep P.
       float P[16], PF[16], PT[16], DS[16], g[16];
-      if constexpr (DROP) drop_row16(a, wk.bh, row, t * TS + sub * 32, g);
+      if constexpr (DROP) dm.get(a, sub, g);
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
@@ -817,6 +902,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const T* uqr = qr + 2 * S::ELEMS;
     const T* uqt = uqr + S::ROW_ELEMS;
     const float* sc = scl[u & 1];
+    DropCol<NSUB> dm;
+    if constexpr (DROP) dm.init(a, (int64_t)wk.b * a.H + wk.h + u / ntq, t * TS, col);
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       const f32x16 s = mm_row<T, D, TS>(qr, sub, kf, query_init<TS, CAUSAL>(sc, sub, t * TS, col));
@@ -828,7 +915,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       f32x16 c = mm_row<T, D, TS>(dr, sub, uvf, DROP ? zero16() : row_init<TS>(sc + 3 * TS, sub));
       float g[16];
       if constexpr (DROP) {
-        drop_col16(a, (int64_t)wk.b * a.H + wk.h + u / ntq, t * TS + sub * 32, col, g);
+        dm.get(a, sub, g);
         const f32x16 nd = row_init<TS>(sc + TS, sub), nc = row_init<TS>(sc + 3 * TS, sub);
 #pragma unroll
         for (int idx = 0; idx < 16; ++idx) {

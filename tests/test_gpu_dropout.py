@@ -35,6 +35,8 @@ def run_dropout(t, p, seed, causal):
     (1, 2, 2, 100, 64, "fp32", 0.1, False),   # ragged tile
     (1, 1, 1, 128, 64, "fp32", 0.5, True),
     (1, 2, 2, 130, 64, "bf16", 0.25, False),  # ragged resident block
+    (1, 2, 2, 300, 64, "bf16", 0.3, False),   # several key tiles and resident blocks
+    (1, 1, 1, 290, 128, "bf16", 0.3, True),
     (2, 2, 2, 97, 64, "bf16", 0.5, True),
     (1, 4, 2, 64, 64, "bf16", 0.1, False),    # grouped-query heads
     (1, 2, 2, 75, 128, "bf16", 0.2, False),   # d = 128
