@@ -365,7 +365,9 @@ def main():
         r = Runner(w, dropout=args.dropout, seed=1234)
         d_ms = time_plain(r.bob, reps_for(settle(r.bob)))
         dropout_leg = {"p": args.dropout, "workload": w.name, "fa_bob_ms": round(d_ms, 4),
-                       "tflops": round(w.bob_flops / (d_ms * 1e9), 1), "kernels": "portable, mask from Philox4x64-10"}
+                       "tflops": round(w.bob_flops / (d_ms * 1e9), 1),
+                       "kernels": ("LDS-DMA row pass and split-schedule column pass" if w.dtype == "bf16"
+                                   else "portable") + ", mask from Philox4x64-10"}
 
     line = {
         "metric": "fa_bob TFLOP/s (38 B H N^2 d flops per call) and fraction of bf16 dense MFMA peak",

@@ -219,7 +219,24 @@ template <typename T, int D, bool RHO1, bool C>
 void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int phase) {
   const dim3 g(grid_rows(c)), b(fa::kThreads), gc(grid_cols(c));
   auto want = [&](int ph) { return phase < 0 || phase == ph; };
-  if (c.drop) {  // two-pass schedule on the portable kernels (schedule 2 is refused earlier)
+  if (c.drop) {  // two-pass schedule (schedule 2 is refused earlier)
+    if constexpr (sizeof(T) == 2) {
+      // bf16: the LDS-DMA row pass (which computes D itself) and the column
+      // pass's split schedule, both with the mask.
+      if (want(1)) {
+        if constexpr (D == 64)
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C, 0, true>), g, b, 0, st, a);
+        else
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C, 0, true>), g, b, 0, st, a);
+      }
+      if (want(2)) {
+        if constexpr (D == 64)
+          hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, true, false, C, true>), gc, b, 0, st, a);
+        else
+          hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C, true>), gc, b, 0, st, a);
+      }
+      return;
+    }
     if (want(0)) launch_rowscalar<T, D>(c, a, st);
     if (want(1)) hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), g, b, 0, st, a);
     if (want(2)) hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), gc, b, 0, st, a);

@@ -141,8 +141,17 @@ __device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
 //   G  += P U_V + (P h) V        (= gdo, no correction),
 //   Om += (P d~P) K + dS U_K,    Bk += P K,      gq = tau (Om - E Bk)
 // (the delayed E-correction), with one accumulation fewer than SCHED = 0.
-template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL, int SCHED = 0>
+//
+// DROP (two-pass only): dropout with the forward's scaled keep mask g
+// ([FlashBoB] appendix G, analytical dropout extension): dP and C become
+// g dP and g C, and the products with V and U_V (the accumulator G) take
+// P g and P F g; alpha, E°, Om, R' and Bk keep P.  The mask of each pair of
+// sub-tiles comes from one shared generator call per lane (DropRow), issued
+// while the score MFMAs of the first of them are in flight.
+template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL, int SCHED = 0, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_dma_kernel(Args a) {
+  static_assert(!(DROP && SCHED != 0), "the three-pass schedule has no dropout variant");
+  static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int NSLICE = 2 * NDB;  // (d-block, k-step) pairs of one accumulation
@@ -245,13 +254,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
     // One (d-block, k-step) slice of the accumulations of sub-tile `sub`.
+    // With DROP, cpf carries P F g and cpg P g (the operands of G).
     auto acc_slice = [&](int sub, int db, int s2, const Chain<bf16>& cp, const Chain<bf16>& cpf,
-                         const Chain<bf16>& cpt, const Chain<bf16>& cds) {
+                         const Chain<bf16>& cpt, const Chain<bf16>& cds, const Chain<bf16>& cpg) {
       const bf16x8 xuv = rd_tr<D, TS>(tuv, rd, sub, db, s2);
       const bf16x8 xv = rd_tr<D, TS>(tv, rd, sub, db, s2);
       const bf16x8 xk = rd_tr<D, TS>(tk, rd, sub, db, s2);
       const bf16x8 xuk = rd_tr<D, TS>(tuk, rd, sub, db, s2);
-      mfma_acc(ag[db], xuv, cp.f[s2]);
+      mfma_acc(ag[db], xuv, DROP ? cpg.f[s2] : cp.f[s2]);
       mfma_acc(ag[db], xv, cpf.f[s2]);
       mfma_acc(aom[db], xk, cpt.f[s2]);
       mfma_acc(aom[db], xuk, cds.f[s2]);
@@ -260,12 +270,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     // Elementwise work on elements 4*part .. 4*part+3 of the current sub-tile.
     auto elementwise = [&](int part, const f32x16& s, const f32x16& f, const f32x16& dp, const f32x16& c,
-                           Chain<bf16>& cp, Chain<bf16>& cpf, Chain<bf16>& cpt, Chain<bf16>& cds) {
+                           Chain<bf16>& cp, Chain<bf16>& cpf, Chain<bf16>& cpt, Chain<bf16>& cds, Chain<bf16>& cpg,
+                           const DropRow<2>& dm, int gsub) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = 4 * part + e;
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
         const float F = RHO1 ? f[idx] : f[idx] * a.rho;
+        if constexpr (DROP) {
+          const float g = dm.at(a, gsub, idx);
+          const float dpd = fmaf(g, dp[idx], -Di);
+          const float pf = p * F, pt = p * fmaf(F, dpd, g * c[idx]);
+          alpha_p += pf;
+          eo_p += pt;
+          const bf16 ptb = (bf16)pt;
+          eob_p += (float)ptb;
+          cp.f[idx >> 3][idx & 7] = (bf16)p;
+          cpf.f[idx >> 3][idx & 7] = (bf16)(pf * g);
+          cpt.f[idx >> 3][idx & 7] = ptb;
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dpd);
+          cpg.f[idx >> 3][idx & 7] = (bf16)(p * g);
+          continue;
+        }
         const float dpd = dp[idx] - Di;
         const float t0 = fmaf(F, dpd, c[idx]);
         if constexpr (SCHED == 0) {
@@ -294,14 +320,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     f32x16 s, f, dp, c;
     scores(0, s, f, dp, c);
-    Chain<bf16> pp, ppf, ppt, pds;  // chains of the previous sub-tile
+    Chain<bf16> pp, ppf, ppt, pds, ppg;  // chains of the previous sub-tile
+    DropRow<2> dm;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
+      if constexpr (DROP) {
+        if (sub % 2 == 0) dm.init(a, wk.bh, row, t * TS + sub * 32);
+      }
       mfma_fence(s, f, dp, c);
-      Chain<bf16> cp, cpf, cpt, cds;
+      Chain<bf16> cp, cpf, cpt, cds, cpg;
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
-        elementwise(part, s, f, dp, c, cp, cpf, cpt, cds);
+        elementwise(part, s, f, dp, c, cp, cpf, cpt, cds, cpg, dm, sub & 1);
         if constexpr (SPLIT) {
           // Parts 0-1 overlap the k-step-1 half of sub - 1; parts 2-3 the
           // k-step-0 half of this sub-tile (its chains come from parts 0-1).
@@ -309,30 +339,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           if (part < 2) {
             if (sub > 0) {
 #pragma unroll
-              for (int db = part * H; db < (part + 1) * H; ++db) acc_slice(sub - 1, db, 1, pp, ppf, ppt, pds);
+              for (int db = part * H; db < (part + 1) * H; ++db) acc_slice(sub - 1, db, 1, pp, ppf, ppt, pds, ppg);
             }
           } else {
 #pragma unroll
-            for (int db = (part - 2) * H; db < (part - 1) * H; ++db) acc_slice(sub, db, 0, cp, cpf, cpt, cds);
+            for (int db = (part - 2) * H; db < (part - 1) * H; ++db) acc_slice(sub, db, 0, cp, cpf, cpt, cds, cpg);
           }
         } else if (sub > 0) {
 #pragma unroll
           for (int sl = part * NSLICE / 4; sl < (part + 1) * NSLICE / 4; ++sl)
-            acc_slice(sub - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds);
+            acc_slice(sub - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds, ppg);
         }
       }
       pp = cp;
       ppf = cpf;
       ppt = cpt;
       pds = cds;
+      if constexpr (DROP) ppg = cpg;
       if (sub + 1 < NSUB) scores(sub + 1, s, f, dp, c);
     }
     if constexpr (SPLIT) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_slice(NSUB - 1, db, 1, pp, ppf, ppt, pds);
+      for (int db = 0; db < NDB; ++db) acc_slice(NSUB - 1, db, 1, pp, ppf, ppt, pds, ppg);
     } else {
 #pragma unroll
-      for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds);
+      for (int sl = 0; sl < NSLICE; ++sl) acc_slice(NSUB - 1, sl >> 1, sl & 1, pp, ppf, ppt, pds, ppg);
     }
   };
 
@@ -529,8 +560,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //   d~S = P (d~P - E),    dS = P dPD,    W = P h,
 //   gk += d~S^T Q + dS^T U_Q (times tau at the end),  gv += W^T dO.
 // Same tile schedule as pass 1.
-template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL>
+//
+// DROP (split schedule only): dropout with the forward's scaled keep mask g
+// ([FlashBoB] appendix G, analytical dropout extension): dP = g (dO V^T) - D
+// and C' = g (dO U_V^T) - alpha D - E, so these two chains start at 0 and take
+// their staged scalars after the mask; W = P g h.  The mask of each pair of
+// sub-tiles comes from one shared generator call per lane (DropCol).
+template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_dma_kernel(Args a) {
+  static_assert(!DROP || (SPLIT && TS % 64 == 0), "dropout runs the split schedule on pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int NSLICE = 2 * NDB;
@@ -608,7 +646,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Tile modes: 0 = rows masked only through the staged inits, 2 = causal
   // diagonal tile (also -inf where query < key).
   // Tile t in LDS buffer buf.
-  auto tile_body = [&](int t, int buf, auto mode_c) {
+  // Tile t of query head wk.h + gq in LDS buffer buf.
+  auto tile_body = [&](int t, int buf, int gq, auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
     const char* tq = lds + buf * STAGE;
     const char* tdo = tq + W::BYTES;
@@ -623,9 +662,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           if (t * TS + sub * 32 + acc_pos(idx, hh) < col) s[idx] = -INFINITY;
         asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
       }
-      dp = row_init<TS>(sc + TS, sub);
+      dp = DROP ? zero16() : row_init<TS>(sc + TS, sub);
       f = row_init<TS>(sc + 2 * TS, sub);
-      c = row_init<TS>(sc + 3 * TS, sub);
+      c = DROP ? zero16() : row_init<TS>(sc + 3 * TS, sub);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 xq = rd_row<D, TS>(tq, rd, sub, ks);
@@ -652,13 +691,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       mfma_acc(ak[db], xuq, cds.f[s2]);
       mfma_acc(av[db], xd, cw.f[s2]);
     };
+    // With DROP, nd and nc hold the staged -D and -(alpha D + E) of the
+    // sub-tile's rows and dm its mask.
     auto elementwise = [&](int part, const f32x16& s, const f32x16& f, const f32x16& dp, const f32x16& c,
-                           Chain<bf16>& cdt, Chain<bf16>& cds, Chain<bf16>& cw) {
+                           Chain<bf16>& cdt, Chain<bf16>& cds, Chain<bf16>& cw, const f32x16& nd,
+                           const f32x16& nc, const DropCol<2>& dm, int gsub) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = 4 * part + e;
         const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
         const float h = RHO1 ? f[idx] : f[idx] * a.rho;
+        if constexpr (DROP) {
+          const float g = dm.at(a, gsub, idx);
+          const float dpx = fmaf(g, dp[idx], nd[idx]);
+          cdt.f[idx >> 3][idx & 7] = (bf16)(p * fmaf(h, dpx, fmaf(g, c[idx], nc[idx])));
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dpx);
+          cw.f[idx >> 3][idx & 7] = (bf16)(p * g * h);
+          continue;
+        }
         const float x = fmaf(h, dp[idx], c[idx]);
         cdt.f[idx >> 3][idx & 7] = (bf16)(p * x);
         cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
@@ -869,13 +919,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     f32x16 s, f, dp, c;
     scores(0, s, f, dp, c);
     Chain<bf16> pdt, pds, pw;  // chains of the previous sub-tile
+    DropCol<2> dm;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
+      f32x16 nd, nc;
+      if constexpr (DROP) {
+        if (sub % 2 == 0) dm.init(a, (int64_t)wk.b * a.H + wk.h + gq, t * TS + sub * 32, col);
+        nd = row_init<TS>(sc + TS, sub);
+        nc = row_init<TS>(sc + 3 * TS, sub);
+      }
       mfma_fence(s, f, dp, c);
       Chain<bf16> cdt, cds, cw;
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
-        elementwise(part, s, f, dp, c, cdt, cds, cw);
+        elementwise(part, s, f, dp, c, cdt, cds, cw, nd, nc, dm, sub & 1);
         if constexpr (SPLIT) {
           constexpr int H = NDB / 2;
           if (part < 2) {
@@ -913,7 +970,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool wrap = t + 1 >= nt;
         const int gn = wrap ? g + 1 : g, tn = wrap ? t_begin : t + 1;
         if (gn < a.G) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
-        tile_body(t, u & 1, mode_c);
+        tile_body(t, u & 1, g, mode_c);
         ++u;
       }
       acc_fence2<NDB>(ak, av);

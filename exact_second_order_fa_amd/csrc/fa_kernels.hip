@@ -137,13 +137,26 @@ struct ScalarStager {
 struct U64x4 {
   uint64_t w0, w1, w2, w3;
 };
+// High and low words of the 128-bit product a * m from four 32 x 32 -> 64-bit
+// partial products, each one v_mad_u64_u32 with the carry of the previous one
+// as its addend (none of the sums can exceed 64 bits).
+__device__ inline void mulhilo64(uint64_t a, uint64_t m, uint64_t& hi, uint64_t& lo) {
+  const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32), m0 = (uint32_t)m, m1 = (uint32_t)(m >> 32);
+  const uint64_t p00 = (uint64_t)a0 * m0;
+  const uint64_t p01 = (uint64_t)a0 * m1 + (p00 >> 32);
+  const uint64_t p10 = (uint64_t)a1 * m0 + (uint32_t)p01;
+  const uint64_t p11 = (uint64_t)a1 * m1 + (p01 >> 32);
+  lo = (p10 << 32) | (uint32_t)p00;
+  hi = p11 + (p10 >> 32);
+}
 __device__ inline U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3, uint64_t k0, uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
-    const uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(c0, M0, hi0, lo0);
+    mulhilo64(c2, M1, hi1, lo1);
     c0 = hi1 ^ c1 ^ k0;
     c1 = lo1;
     c2 = hi0 ^ c3 ^ k1;
@@ -206,8 +219,8 @@ struct DropRow {
   __device__ inline void init(const Args& a, int64_t bh, int i, int s0) {
     const int hh = lane_id() >> 5, r = lane_id() & 3;
     const int sub = NS == 2 ? r >> 1 : 0;
-    const U64x4 x = philox4x64_10((uint64_t)(i >> 2), (uint64_t)(s0 / 8 + 4 * sub + 2 * (r & 1) + hh), (uint64_t)bh,
-                                  0, a.seed, 0);
+    const U64x4 x = philox4x64_10((uint32_t)(i >> 2), (uint32_t)(s0 / 8 + 4 * sub + 2 * (r & 1) + hh),
+                                  (uint32_t)bh, 0, a.seed, 0);
     const uint64_t ww[4] = {x.w0, x.w1, x.w2, x.w3};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -216,13 +229,14 @@ struct DropRow {
     }
     xor_transpose<4, 2>(w);
   }
+  // g of element idx (0..15) of sub-tile sub of the granule.
+  __device__ inline float at(const Args& a, int sub, int idx) const {
+    const int b = idx >> 2;
+    return keep_byte(a, w[(NS == 2 ? 2 * sub : 0) + (b >> 1)][b & 1], idx & 3);
+  }
   __device__ inline void get(const Args& a, int sub, float (&g)[16]) const {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t d = w[(NS == 2 ? 2 * sub : 0) + (b >> 1)][b & 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) g[4 * b + e] = keep_byte(a, d, e);
-    }
+    for (int idx = 0; idx < 16; ++idx) g[idx] = at(a, sub, idx);
   }
 };
 
@@ -240,8 +254,8 @@ struct DropCol {
   __device__ inline void init(const Args& a, int64_t bh, int s0, int j) {
     const int hh = lane_id() >> 5, r = lane_id() & 7;
     const int sub = NS == 2 ? r >> 2 : 0, b = r & 3;
-    const U64x4 x = philox4x64_10((uint64_t)(s0 / 4 + 8 * sub + 4 * (b >> 1) + 2 * hh + (b & 1)),
-                                  (uint64_t)(j >> 3), (uint64_t)bh, 0, a.seed, 0);
+    const U64x4 x = philox4x64_10((uint32_t)(s0 / 4 + 8 * sub + 4 * (b >> 1) + 2 * hh + (b & 1)),
+                                  (uint32_t)(j >> 3), (uint32_t)bh, 0, a.seed, 0);
     const uint64_t ww[4] = {x.w0, x.w1, x.w2, x.w3};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -252,13 +266,13 @@ struct DropCol {
     }
     xor_transpose<8, 1>(w);
   }
+  // g of element idx (0..15) of sub-tile sub of the granule.
+  __device__ inline float at(const Args& a, int sub, int idx) const {
+    return keep_byte(a, w[(NS == 2 ? 4 * sub : 0) + (idx >> 2)][0], idx & 3);
+  }
   __device__ inline void get(const Args& a, int sub, float (&g)[16]) const {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t d = w[(NS == 2 ? 4 * sub : 0) + b][0];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) g[4 * b + e] = keep_byte(a, d, e);
-    }
+    for (int idx = 0; idx < 16; ++idx) g[idx] = at(a, sub, idx);
   }
 };
 
