@@ -356,8 +356,8 @@ def main():
         if name in PAGES_MS:
             sweep[name]["pages_ms_context"] = PAGES_MS[name]
 
-    # The dropout variant ([FlashBoB] appendix G) on the same workload: the
-    # portable kernels with the Philox mask, reported beside the headline.
+    # The dropout variant ([FlashBoB] appendix G) on the same workload, with
+    # the Philox mask, reported beside the headline.
     dropout_leg = None
     if args.dropout > 0:
         del r
