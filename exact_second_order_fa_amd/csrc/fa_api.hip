@@ -165,23 +165,27 @@ struct Tiles {
   static constexpr int TS = (sizeof(T) == 2 && D == 64) ? 64 : 32;
 };
 
-// Dropout runs on the portable kernels (register-staged tiles, one wave per
-// SIMD) for every input type; the tuned bf16 kernels carry no mask.
+// Dropout: the LDS-DMA kernels with their DROP flag for bf16 inputs, the
+// portable kernels (register-staged tiles, one wave per SIMD) for fp32.
 template <typename T, int D, bool C>
 void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
-  if (c.drop)
+  if constexpr (sizeof(T) == 2) {
+    if (c.drop)
+      hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C, true>), dim3(grid_rows(c)),
+                         dim3(fa::kThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
+                         st, a);
+  } else if (c.drop)
     hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
                        st, a);
-  else if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
-                       a);
   else
     hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
 }
 
 template <typename T, int D, bool C>
 void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
-  if (c.drop) {
+  if (sizeof(T) != 2 && c.drop) {
     Args b = a;
     b.bs = nullptr;
     launch_rowscalar<T, D>(c, b, st);
@@ -195,8 +199,14 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
     // Row scalars D plus the staged chain inits (-L/rho, -D) of the column kernel.
     hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c, true)), dim3(256), 0, st, a);
     constexpr int TS = D == 64 ? 128 : 64;
-    hipLaunchKernelGGL((fa::bwd_dq_dma_kernel<D, TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
-    hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0, st, a);
+    if (c.drop) {
+      hipLaunchKernelGGL((fa::bwd_dq_dma_kernel<D, TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C, true>), dim3(grid_cols(c)), dim3(fa::kThreads), 0, st,
+                         a);
+    } else {
+      hipLaunchKernelGGL((fa::bwd_dq_dma_kernel<D, TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0, st, a);
+    }
   } else {
     Args b = a;
     b.bs = nullptr;

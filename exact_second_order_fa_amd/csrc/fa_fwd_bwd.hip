@@ -40,8 +40,14 @@ __device__ inline f32x16 mfma_first_a(bf16x8 a, bf16x8 b) {
 // skipped when no row's maximum moved, which after the first tiles is the
 // common case.  The scores of sub-tile s + 1 are issued before the
 // elementwise work of s, so the matrix cores and the VALU overlap.
-template <int D, int TS, bool CAUSAL>
+//
+// DROP: dropout with the scaled keep mask g ([FlashBoB] appendix G): O takes
+// (P g) V while the row sum and L keep P.  The mask of each pair of sub-tiles
+// comes from one shared generator call per lane (DropRow), issued behind the
+// score MFMAs of the next sub-tile.
+template <int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_dma_kernel(Args a) {
+  static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int STAGE = 2 * W::BYTES;
@@ -101,11 +107,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     f32x16 sb[2];
     scores(0, sb[0]);
+    DropRow<2> dm;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       f32x16& s = sb[sub & 1];
       vfence1(s);
       if (sub + 1 < NSUB) scores(sub + 1, sb[(sub + 1) & 1]);
+      if constexpr (DROP) {
+        if (sub % 2 == 0) dm.init(a, wk.bh, row, t * TS + sub * 32);
+      }
       float mx = s[0];
 #pragma unroll
       for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, s[idx]);
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], c1, -ms));
         ps += p;
-        cp.f[idx >> 3][idx & 7] = (bf16)p;
+        cp.f[idx >> 3][idx & 7] = (bf16)(DROP ? p * dm.at(a, sub & 1, idx) : p);
       }
       lsum = fmaf(lsum, sc, ps);
       m = mn;
@@ -166,9 +176,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // First backward, row side: dQ = tau dS K with dS = P (dP - D).  Resident per
 // wave: q_i (scaled by pow2), do_i, L_i, D_i; streamed K, V.  Per 32-key
 // sub-tile: S^T = K Q^T and dP^T = V dO^T (keys on M), P = exp(tau S - L),
-// dS = P (dP - D), and dQ^T += K^T dS^T (transposed K from LDS).
-template <int D, int TS, bool CAUSAL>
+// dS = P (dP - D), and dQ^T += K^T dS^T (transposed K from LDS).  DROP: dP is
+// g (dO V^T) ([FlashBoB] appendix G), so dS = P (g dP - D).
+template <int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_dma_kernel(Args a) {
+  static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int STAGE = 2 * W::BYTES;
@@ -244,17 +256,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     f32x16 sb[2], pb[2];
     scores(0, sb[0], pb[0]);
+    DropRow<2> dm;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       f32x16& s = sb[sub & 1];
       f32x16& dp = pb[sub & 1];
       asm volatile("s_nop 7\n\ts_nop 4" : "+v"(s), "+v"(dp));  // MFMA result -> VALU read
       if (sub + 1 < NSUB) scores(sub + 1, sb[(sub + 1) & 1], pb[(sub + 1) & 1]);
+      if constexpr (DROP) {
+        if (sub % 2 == 0) dm.init(a, wk.bh, row, t * TS + sub * 32);
+      }
       Chain<bf16> cds;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
-        cds.f[idx >> 3][idx & 7] = (bf16)(p * (dp[idx] - Di));
+        cds.f[idx >> 3][idx & 7] = (bf16)(p * (DROP ? fmaf(dm.at(a, sub & 1, idx), dp[idx], -Di) : dp[idx] - Di));
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -291,8 +307,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // sub-tile (queries on M): S = Q K^T, dP - D = dO V^T - D, P = exp(tau S - L),
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  The G query heads of a
 // key/value head are streamed one after another into the same accumulators.
-template <int D, int TS, bool CAUSAL>
+// DROP ([FlashBoB] appendix G): dP - D = g (dO V^T) - D, so that chain starts
+// at 0 and takes -D after the mask, and dV^T += dO^T (P g).
+template <int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_dma_kernel(Args a) {
+  static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int TBYTES = 2 * W::BYTES;
@@ -346,7 +365,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-  auto tile_body = [&](int t, int buf, auto mode_c) {
+  // Tile t of query head wk.h + gq in LDS buffer buf.
+  auto tile_body = [&](int t, int buf, int gq, auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
     const char* tq = lds + buf * STAGE;
     const char* tdo = tq + W::BYTES;
@@ -358,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int idx = 0; idx < 16; ++idx)
           if (t * TS + sub * 32 + acc_pos(idx, hh) < col) s[idx] = -INFINITY;
       }
-      dp = row_init<TS>(sc + TS, sub);
+      dp = DROP ? zero16() : row_init<TS>(sc + TS, sub);
       asm volatile("s_nop 1" : "+v"(s), "+v"(dp));  // VALU write -> MFMA read of C
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -368,18 +388,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     f32x16 sb[2], pb[2];
     scores(0, sb[0], pb[0]);
+    DropCol<2> dm;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
       f32x16& s = sb[sub & 1];
       f32x16& dp = pb[sub & 1];
       asm volatile("s_nop 7\n\ts_nop 4" : "+v"(s), "+v"(dp));  // MFMA result -> VALU read
       if (sub + 1 < NSUB) scores(sub + 1, sb[(sub + 1) & 1], pb[(sub + 1) & 1]);
+      f32x16 nd;
+      if constexpr (DROP) {
+        if (sub % 2 == 0) dm.init(a, (int64_t)wk.b * a.H + wk.h + gq, t * TS + sub * 32, col);
+        nd = row_init<TS>(sc + TS, sub);
+      }
       Chain<bf16> cp, cds;
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
-        cp.f[idx >> 3][idx & 7] = (bf16)p;
-        cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
+        if constexpr (DROP) {
+          const float g = dm.at(a, sub & 1, idx);
+          cp.f[idx >> 3][idx & 7] = (bf16)(p * g);
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * fmaf(g, dp[idx], nd[idx]));
+        } else {
+          cp.f[idx >> 3][idx & 7] = (bf16)p;
+          cds.f[idx >> 3][idx & 7] = (bf16)(p * dp[idx]);
+        }
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -400,7 +432,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool wrap = t + 1 >= nt;
         const int gn = wrap ? g + 1 : g, tn = wrap ? t_begin : t + 1;
         if (gn < a.G) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
-        tile_body(t, u & 1, mode_c);
+        tile_body(t, u & 1, g, mode_c);
         ++u;
       }
       acc_fence2<NDB>(ak, av);
