@@ -185,15 +185,17 @@ void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
 
 template <typename T, int D, bool C>
 void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
-  if (sizeof(T) != 2 && c.drop) {
-    Args b = a;
-    b.bs = nullptr;
-    launch_rowscalar<T, D>(c, b, st);
-    hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads),
-                       0, st, b);
-    hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_cols(c)),
-                       dim3(fa::kThreads), 0, st, b);
-    return;
+  if constexpr (sizeof(T) != 2) {
+    if (c.drop) {
+      Args b = a;
+      b.bs = nullptr;
+      launch_rowscalar<T, D>(c, b, st);
+      hipLaunchKernelGGL((fa::bwd_dq_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_rows(c)),
+                         dim3(fa::kThreads), 0, st, b);
+      hipLaunchKernelGGL((fa::bwd_dkdv_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_cols(c)),
+                         dim3(fa::kThreads), 0, st, b);
+      return;
+    }
   }
   if constexpr (sizeof(T) == 2) {
     // Row scalars D plus the staged chain inits (-L/rho, -D) of the column kernel.
@@ -245,11 +247,11 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
         else
           hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C, true>), gc, b, 0, st, a);
       }
-      return;
+    } else {
+      if (want(0)) launch_rowscalar<T, D>(c, a, st);
+      if (want(1)) hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), g, b, 0, st, a);
+      if (want(2)) hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), gc, b, 0, st, a);
     }
-    if (want(0)) launch_rowscalar<T, D>(c, a, st);
-    if (want(1)) hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), g, b, 0, st, a);
-    if (want(2)) hipLaunchKernelGGL((fa::bob_pass2_kernel<T, D, Tiles<T, D>::TS, RHO1, C, true>), gc, b, 0, st, a);
     return;
   }
   // The bf16 two-pass row passes compute D themselves; phase 0 then launches nothing.
