@@ -40,22 +40,22 @@ __device__ inline void fill_bias(float* b, int row0, int N) {
 //     tied destination here, so the fence above covers it);
 //   * back-to-back accumulation into the same registers needs none.
 
-// f(integral_constant<int, i>) for i = B .. E - 1, in order: the index is a
-// compile-time constant inside f, whatever the unroller decides.
-template <int B, int... I, typename F>
-__device__ inline void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
-  (f(std::integral_constant<int, B + I>{}), ...);
-}
-template <int B, int E, typename F>
-__device__ inline void static_for(F&& f) {
-  if constexpr (E > B) static_for_impl<B>(std::make_integer_sequence<int, E - B>{}, f);
-}
-
 // d = a * b (a chain start; C = 0).
 __device__ inline f32x16 mfma_first(bf16x8 a, bf16x8 b) {
   f32x16 d;
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
+}
+// The same two with the two wait states of a VALU write in front: for kernels
+// where the compiler, short of VGPRs, may copy a resident B operand back from
+// AGPRs (v_accvgpr_read, a VALU instruction) right before the MFMA.
+__device__ inline f32x16 mfma_first_w(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ inline void mfma_v_w(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 // d += a * b, d in VGPRs, b resident in AGPRs.
 __device__ inline void mfma_va(f32x16& d, bf16x8 a, bf16x8 b) {
@@ -221,6 +221,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const char* tuk = tk + 2 * W::BYTES;
     const char* tuv = tk + 3 * W::BYTES;
 
+    // The dropout instance runs short of VGPRs: its score MFMAs carry the
+    // wait states of a VALU write themselves (see mfma_first_w).
+    auto first = [&](bf16x8 x, bf16x8 y) { return DROP ? mfma_first_w(x, y) : mfma_first(x, y); };
+    auto macc = [&](f32x16& z, bf16x8 x, bf16x8 y) {
+      if constexpr (DROP) {
+        mfma_v_w(z, x, y);
+      } else {
+        mfma_v(z, x, y);
+      }
+    };
     auto scores = [&](int sub, f32x16& s, f32x16& f, f32x16& dp, f32x16& c) {
       if constexpr (MODE == 1) {
         s = row_init<TS>(kbias, sub);
@@ -237,20 +247,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bf16x8 xv = rd_row<D, TS>(tv, rd, sub, ks);
         const bf16x8 xuv = rd_row<D, TS>(tuv, rd, sub, ks);
         if (MODE == 0 && ks == 0) {
-          s = mfma_first(xk, qf[0]);
+          s = first(xk, qf[0]);
         } else {
-          mfma_v(s, xk, qf[ks]);
+          macc(s, xk, qf[ks]);
         }
         if (ks == 0) {
-          f = mfma_first(xk, uqf[0]);
-          dp = mfma_first(xv, df[0]);
-          c = mfma_first(xuv, df[0]);
+          f = first(xk, uqf[0]);
+          dp = first(xv, df[0]);
+          c = first(xuv, df[0]);
         } else {
-          mfma_v(f, xk, uqf[ks]);
-          mfma_v(dp, xv, df[ks]);
-          mfma_v(c, xuv, df[ks]);
+          macc(f, xk, uqf[ks]);
+          macc(dp, xv, df[ks]);
+          macc(c, xuv, df[ks]);
         }
-        mfma_v(f, xuk, qf[ks]);
+        macc(f, xuk, qf[ks]);
       }
     };
     // One (d-block, k-step) slice of the accumulations of sub-tile `sub`.

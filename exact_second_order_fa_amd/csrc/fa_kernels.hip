@@ -187,22 +187,28 @@ __device__ inline float keep_byte(const Args& a, uint32_t w, int byte) {
 // that bit, and re-slots both by the bit of the lane they came from.
 template <int M, int K>
 __device__ inline void xor_transpose(uint32_t (&A)[M][K]) {
+  // Every index is a compile-time constant (static_for), so the array stays
+  // in registers: with loop-variable indices the compiler may place it in LDS
+  // before unrolling, one row per lane, which bank-conflicts.
+  constexpr int LOGM = M == 2 ? 1 : M == 4 ? 2 : 3;
+  static_assert(M == (1 << LOGM), "group of 2, 4 or 8 lanes");
   const int g = lane_id() & (M - 1);
-#pragma unroll
-  for (int bit = 1; bit < M; bit <<= 1) {
+  static_for<0, LOGM>([&](auto bc) {
+    constexpr int bit = 1 << decltype(bc)::value;
     const bool up = (g & bit) != 0;
-#pragma unroll
-    for (int s = 0; s < M; ++s) {
-      if (s & bit) continue;
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const uint32_t send = up ? A[s][k] : A[s | bit][k];
-        const uint32_t recv = (uint32_t)__shfl_xor((int)send, bit);
-        A[s][k] = up ? recv : A[s][k];
-        A[s | bit][k] = up ? A[s | bit][k] : recv;
+    static_for<0, M>([&](auto sc) {
+      constexpr int s = decltype(sc)::value;
+      if constexpr ((s & bit) == 0) {
+        static_for<0, K>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          const uint32_t send = up ? A[s][k] : A[s | bit][k];
+          const uint32_t recv = (uint32_t)__shfl_xor((int)send, bit);
+          A[s][k] = up ? recv : A[s][k];
+          A[s | bit][k] = up ? A[s | bit][k] : recv;
+        });
       }
-    }
-  }
+    });
+  });
 }
 
 // Row side: this lane's query row i (i % 4 = lane % 4) and NS sub-tiles of 32
@@ -222,17 +228,26 @@ struct DropRow {
     const U64x4 x = philox4x64_10((uint32_t)(i >> 2), (uint32_t)(s0 / 8 + 4 * sub + 2 * (r & 1) + hh),
                                   (uint32_t)bh, 0, a.seed, 0);
     const uint64_t ww[4] = {x.w0, x.w1, x.w2, x.w3};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    static_for<0, 4>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
       w[q][0] = (uint32_t)ww[q];
       w[q][1] = (uint32_t)(ww[q] >> 32);
-    }
+    });
     xor_transpose<4, 2>(w);
   }
-  // g of element idx (0..15) of sub-tile sub of the granule.
+  // g of element idx (0..15) of sub-tile sub of the granule.  The word is
+  // picked by selects over constant indices (see xor_transpose).
   __device__ inline float at(const Args& a, int sub, int idx) const {
-    const int b = idx >> 2;
-    return keep_byte(a, w[(NS == 2 ? 2 * sub : 0) + (b >> 1)][b & 1], idx & 3);
+    const int b = idx >> 2, q = (NS == 2 ? 2 * sub : 0) + (b >> 1), h = b & 1;
+    auto wq = [&](auto qc) {
+      constexpr int c = decltype(qc)::value;
+      return h ? w[c][1] : w[c][0];
+    };
+    const uint32_t d = q == 0   ? wq(std::integral_constant<int, 0>{})
+                       : q == 1 ? wq(std::integral_constant<int, 1>{})
+                       : q == 2 ? wq(std::integral_constant<int, 2>{})
+                                : wq(std::integral_constant<int, 3>{});
+    return keep_byte(a, d, idx & 3);
   }
   __device__ inline void get(const Args& a, int sub, float (&g)[16]) const {
 #pragma unroll
@@ -257,18 +272,27 @@ struct DropCol {
     const U64x4 x = philox4x64_10((uint32_t)(s0 / 4 + 8 * sub + 4 * (b >> 1) + 2 * hh + (b & 1)),
                                   (uint32_t)(j >> 3), (uint32_t)bh, 0, a.seed, 0);
     const uint64_t ww[4] = {x.w0, x.w1, x.w2, x.w3};
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    static_for<0, 8>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
       uint32_t item = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) item |= (uint32_t)((ww[e] >> (8 * q)) & 0xffu) << (8 * e);
+      static_for<0, 4>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        item |= (uint32_t)((ww[e] >> (8 * q)) & 0xffu) << (8 * e);
+      });
       w[q][0] = item;
-    }
+    });
     xor_transpose<8, 1>(w);
   }
-  // g of element idx (0..15) of sub-tile sub of the granule.
+  // g of element idx (0..15) of sub-tile sub of the granule.  The word is
+  // picked by selects over constant indices (see xor_transpose).
   __device__ inline float at(const Args& a, int sub, int idx) const {
-    return keep_byte(a, w[(NS == 2 ? 4 * sub : 0) + (idx >> 2)][0], idx & 3);
+    const int q = (NS == 2 ? 4 * sub : 0) + (idx >> 2);
+    uint32_t d = w[0][0];
+    static_for<1, 2 * 4>([&](auto qc) {
+      constexpr int c = decltype(qc)::value;
+      d = q == c ? w[c][0] : d;
+    });
+    return keep_byte(a, d, idx & 3);
   }
   __device__ inline void get(const Args& a, int sub, float (&g)[16]) const {
 #pragma unroll

@@ -25,6 +25,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -85,6 +88,17 @@ struct Elem<float> {
 };
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// f(integral_constant<int, i>) for i = B .. E - 1, in order: the index is a
+// compile-time constant inside f, whatever the unroller decides.
+template <int B, int... I, typename F>
+__device__ inline void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(std::integral_constant<int, B + I>{}), ...);
+}
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (E > B) static_for_impl<B>(std::make_integer_sequence<int, E - B>{}, f);
+}
 
 // Swap bits 2 and 3 (an involution on 0..31).
 __host__ __device__ constexpr int sig(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
