@@ -158,11 +158,11 @@ void launch_rowscalar(const Ctx& c, const Args& a, hipStream_t st) {
   hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c)), dim3(256), 0, st, a);
 }
 
-// Streamed tile rows per LDS stage: one 16-byte register block per thread
-// for the bf16 path.
+// Streamed tile rows per LDS stage of the portable kernels (fp32 inputs).
 template <typename T, int D>
 struct Tiles {
-  static constexpr int TS = (sizeof(T) == 2 && D == 64) ? 64 : 32;
+  static_assert(sizeof(T) == 4, "bf16 inputs run the LDS-DMA kernels");
+  static constexpr int TS = 32;
 };
 
 // Dropout: the LDS-DMA kernels with their DROP flag for bf16 inputs, the
