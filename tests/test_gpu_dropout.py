@@ -41,6 +41,8 @@ def run_dropout(t, p, seed, causal):
     (1, 4, 2, 64, 64, "bf16", 0.1, False),    # grouped-query heads
     (1, 2, 2, 75, 128, "bf16", 0.2, False),   # d = 128
     (1, 1, 1, 33, 128, "bf16", 0.9, True),
+    (1, 2, 2, 2048, 64, "bf16", 0.2, True),     # many key tiles and mask granules
+    (1, 2, 1, 1100, 128, "bf16", 0.15, False),  # grouped-query, d = 128, ragged, many tiles
 ])
 def test_dropout_parity(B, H, Hkv, N, d, dtype, p, causal):
     seed = 1000 + N + d
