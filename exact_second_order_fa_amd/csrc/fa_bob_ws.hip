@@ -42,6 +42,15 @@ __device__ inline f32x16 mfma_vv_first(bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
+// d = a * b + c, with c in its own registers (kept).  The matrix core reads
+// c after issue, so a write of c's registers must wait 7 wait states; the
+// compiler does not know that about an asm MFMA (it may reuse them right
+// after the last one), so the wait is part of the instruction here.
+__device__ inline f32x16 mfma_vv_init(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 6" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
 __device__ inline void vfence4(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
   asm volatile("s_nop 7\n\ts_nop 4" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
@@ -190,6 +199,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float Li = row < N ? a.lse[rv + row] : 0.0f;
     // D = rowsum(dO * O) of this row, computed here and written for the column pass.
     const float Di = resident_rowdot<D>(df, head_of<float>(a.o, bb, hd), row, N);
+    // The dP chains start from -D (the MFMA's C operand), so dP - D comes out
+    // of the matrix core.
+    f32x16 negd;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) negd[e] = -Di;
     const float nl2 = -Li * kLog2e;
     float alpha_p = 0.0f, eo_p = 0.0f;
     rd.init();
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         group(5 * ks + 1);
         sched_fence();
         if (ks == 0) {
-          DP[P] = mfma_vv_first(xv, df[0]);
+          DP[P] = mfma_vv_init(xv, df[0], negd);
         } else {
           mfma_vv(DP[P], xv, df[ks]);
         }
@@ -277,7 +291,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr int P = decltype(Pc)::value;
       const float p = __builtin_amdgcn_exp2f(fmaf(S[P][idx], a.c1, nl2));
       const float Fv = RHO1 ? F[P][idx] : F[P][idx] * a.rho;
-      const float dpd = DP[P][idx] - Di;
+      const float dpd = DP[P][idx];
       const float t0 = fmaf(Fv, dpd, C[P][idx]);
       const float pf = p * Fv, pt = p * t0, ds = p * dpd;
       add_here(alpha_p, pf);
