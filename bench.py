@@ -186,6 +186,31 @@ def time_plain(fn, reps):
     return a.elapsed_time(b) / reps
 
 
+def hvp_leg(r):
+    """One Hessian-vector product through attention ([FlashBoB] section 4.1):
+    the linear loss <O, W> through sdpa_bob, its gradient with create_graph,
+    then the gradient of <(dQ, dK, dV), z>: fa_fwd, fa_bwd and fa_bob through
+    the autograd wrapper, with its elementwise torch ops and Python overhead."""
+    import torch
+
+    from exact_second_order_fa_amd.autograd import sdpa_bob
+
+    w = r.w
+    q, k, v = (r.t[n].detach().clone().requires_grad_(True) for n in ("q", "k", "v"))
+    W = r.t["do"].float()
+    z = [r.t[n].float() for n in ("uq", "uk", "uv")]
+
+    def step():
+        o = sdpa_bob(q, k, v, causal=w.causal)
+        g = torch.autograd.grad((o * W).sum(), (q, k, v), create_graph=True)
+        s_ = sum((gi.float() * zi).sum() for gi, zi in zip(g, z))
+        torch.autograd.grad(s_, (q, k, v))
+
+    ms = time_plain(step, reps_for(settle(step)))
+    return {"workload": w.name, "ms": round(ms, 4), "loss": "linear <O, W>",
+            "calls": "sdpa_bob autograd: fa_fwd, fa_bwd, fa_bob and the loss's elementwise torch ops"}
+
+
 def traffic_for(workload):
     """Per-launch HBM bytes of the row pass from the committed rocprofv3
     counter summary, or None when missing or taken on other kernel code."""
@@ -338,6 +363,7 @@ def main():
     pass1_flops = 22.0 * w.B * w.H * w.N * w.N * w.d
     ach = pass1_flops / (per[1] * 1e9)
     traffic = traffic_for(w.name)
+    hvp = hvp_leg(r)
 
     sweep = {}
     for name in [s for s in args.sweep.split(",") if s]:
@@ -394,6 +420,7 @@ def main():
         "prerequisites": prereq,
         "sweep": sweep,
         "dropout_variant": dropout_leg,
+        "hvp_step": hvp,
     }
     if abl_names:
         del r
