@@ -118,23 +118,30 @@ class Runner:
 
 
 def time_steps(r, steps, warmup):
-    """Warmup, then `steps` timed steps.  Returns (wall ms/step, per-kernel
-    average ms from HIP events recorded on the launch stream)."""
+    """Warmup, then `steps` timed steps of the plain fa_bob call (wall clock,
+    synchronized on both sides: the headline), then `steps` more with the
+    three kernels launched one by one and HIP events recorded on the launch
+    stream around each (the per-kernel breakdown; the events between kernels
+    cost the step about 2 %).  Returns (wall ms/step, per-step ms of the
+    event loop, per-kernel average ms)."""
     import torch
 
     for _ in range(warmup):
         r.bob()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        r.bob()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
     stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = time.perf_counter()
     for s in range(steps):
         ev[s][0].record(stream)
         for ph in range(3):
             r.bob(phase=ph)
             ev[s][ph + 1].record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     per = [float(np.mean([ev[s][ph].elapsed_time(ev[s][ph + 1]) for s in range(steps)])) for ph in range(3)]
     step_ev = float(np.mean([ev[s][0].elapsed_time(ev[s][3]) for s in range(steps)]))
     return wall, step_ev, per
