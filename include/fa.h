@@ -64,14 +64,15 @@ typedef enum fa_status {
   FA_ERR_SHAPE = 2,       /* B, H or N < 1, H_kv not 0 or a divisor of H, or sizes overflow */
   FA_ERR_STRIDE = 3,      /* stride or alignment rule violated */
   FA_ERR_DTYPE = 4,       /* unknown input dtype */
-  FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128}, causal not 0/1, or a non-finite/negative scale */
+  FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128} (fp32 inputs: d = 64 only), causal not 0/1,
+                             a non-finite/negative scale, or a dropout rate outside [0, 255.5/256) */
   FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   FA_ERR_HIP = 7          /* the HIP runtime reported a launch error */
 } fa_status;
 
 typedef enum fa_dtype {
   FA_BF16 = 0, /* bfloat16 inputs; contractions on bf16 MFMA, fp32 accumulate */
-  FA_FP32 = 1  /* fp32 inputs; contractions on fp32 MFMA */
+  FA_FP32 = 1  /* fp32 inputs (d = 64); contractions on fp32 MFMA */
 } fa_dtype;
 
 typedef struct fa_problem {
