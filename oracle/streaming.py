@@ -76,6 +76,10 @@ def _row_strip(q, k, v, do, uq, uk, uv, tau, rows, col_chunk, outputs, causal=Fa
     Q, dO, UQ = q[rows], do[rows], uq[rows]
     R = Q.shape[0]
     chunks = _chunks(N, col_chunk)
+    if causal:
+        # A chunk whose keys all lie above every row of the strip is masked
+        # throughout: P = 0 there, so it adds exact zeros to every sum.
+        chunks = [(a, b) for a, b in chunks if a <= int(np.max(rows))]
 
     def scores(a, b):
         S = tau * (Q @ k[a:b].T)
@@ -174,7 +178,10 @@ def _col_strip(q, k, v, do, uq, uk, uv, tau, L, D, alpha, E, cols, row_chunk, ca
     gV = np.zeros((Cn, d))
     dK = np.zeros((Cn, d))
     dV = np.zeros((Cn, d))
+    first_col = int(np.min(cols))
     for a, b in _chunks(N, row_chunk):
+        if causal and b - 1 < first_col:
+            continue  # every row of the chunk precedes every column: P = 0
         Qi, dOi, UQi = q[a:b], do[a:b], uq[a:b]
         La, Da, Aa, Ea = L[a:b, None], D[a:b, None], alpha[a:b, None], E[a:b, None]
         S = tau * (Qi @ Kc.T)
