@@ -21,6 +21,7 @@ Recipe (the same on every machine, since numpy's PCG64 stream is portable):
 from .gen import (  # noqa: F401
     NAMES,
     Workload,
+    MQA_SWEEP,
     WORKLOADS,
     bf16_bits_to_f32,
     f32_to_bf16_bits,

@@ -66,6 +66,20 @@ WORKLOADS = {
     # N from 2K to 128K); no mask or input distribution is stated for it.
     "mqa_32k": Workload("mqa_32k", 1, 8, 32768, 64, "bf16", 8, H_kv=1),
 }
+# The rest of that multi-query range, at both head dims: N = 2K, 8K, 32K, 128K.
+_MQA_SEED = 9
+for _d in (64, 128):
+    for _n in (2048, 8192, 32768, 131072):
+        _name = f"mqa{'' if _d == 64 else '128'}_{_n // 1024}k"
+        if _name not in WORKLOADS:
+            WORKLOADS[_name] = Workload(_name, 1, 8, _n, _d, "bf16", _MQA_SEED, H_kv=1)
+            _MQA_SEED += 1
+# The schedule ablation's longer lengths (the pages' three-pass vs two-pass
+# table runs the causal isolated-layer shape, batch 4 and 12 heads, from 1K to
+# 262K).
+WORKLOADS["gpt2c_64k"] = Workload("gpt2c_64k", 4, 12, 65536, 64, "bf16", 16, causal=True)
+WORKLOADS["gpt2c_256k"] = Workload("gpt2c_256k", 4, 12, 262144, 64, "bf16", 17, causal=True)
+MQA_SWEEP = tuple(sorted((n for n in WORKLOADS if n.startswith("mqa")), key=lambda n: (WORKLOADS[n].d, WORKLOADS[n].N)))
 
 
 def workload(name: str) -> Workload:

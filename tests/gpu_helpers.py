@@ -70,6 +70,22 @@ def run_path(t, scale=None, with_bwd=True, layout="bhnd", causal=False, schedule
     return res
 
 
+def run_dropout(t, p, seed, causal):
+    """fa_fwd, fa_bwd and fa_bob with dropout rate p and generator key seed."""
+    import torch
+
+    import exact_second_order_fa_amd as fa
+
+    kw = dict(causal=causal, dropout=p, seed=seed)
+    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], **kw)
+    dq, dk, dv, _ = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], **kw)
+    gq, gk, gv, gdo, ws = fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"], **kw)
+    B, H, N, _ = t["q"].shape
+    D, alpha, E = fa.split_workspace(ws, B, H, N)
+    torch.cuda.synchronize()
+    return dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv, D=D, alpha=alpha, E=E, gQ=gq, gK=gk, gV=gv, gdO=gdo)
+
+
 def rel(got, ref):
     """max |got - ref| / max |ref| (all-zero references compare absolutely)."""
     got = np.asarray(got, dtype=np.float64)

@@ -8,27 +8,12 @@ import pytest
 
 from fa_inputs import make_inputs
 from oracle import bob_dropout_heads
-from tests.gpu_helpers import host, rel, say, to_device
+from tests.gpu_helpers import host, rel, run_dropout, say, to_device
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": 2e-2, "fp32": 1e-4}
 ALL = ("O", "L", "dQ", "dK", "dV", "D", "alpha", "E", "gQ", "gK", "gV", "gdO")
-
-
-def run_dropout(t, p, seed, causal):
-    import torch
-
-    import exact_second_order_fa_amd as fa
-
-    kw = dict(causal=causal, dropout=p, seed=seed)
-    o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], **kw)
-    dq, dk, dv, _ = fa.fa_bwd(t["q"], t["k"], t["v"], o, lse, t["do"], **kw)
-    gq, gk, gv, gdo, ws = fa.fa_bob(t["q"], t["k"], t["v"], o, lse, t["do"], t["uq"], t["uk"], t["uv"], **kw)
-    B, H, N, _ = t["q"].shape
-    D, alpha, E = fa.split_workspace(ws, B, H, N)
-    torch.cuda.synchronize()
-    return dict(O=o, L=lse, dQ=dq, dK=dk, dV=dv, D=D, alpha=alpha, E=E, gQ=gq, gK=gk, gV=gv, gdO=gdo)
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,d,dtype,p,causal", [
