@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import warnings
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
@@ -117,9 +118,15 @@ def _torch():
 def problem(B, H, N, d, in_dtype=FA_BF16, scale=None, causal=0, H_kv=0, dropout=0.0, seed=0) -> FaProblem:
     """H: query heads; H_kv: key/value heads (0 = H; otherwise a divisor of H);
     dropout: rate p in [0, 1) with generator key ``seed`` (the same pair for
-    fa_fwd, fa_bwd and fa_bob)."""
+    fa_fwd, fa_bwd and fa_bob).  The library keeps an element with
+    probability 1 - t/256, t = round(256 p): p is used as the nearest
+    multiple of 1/256 (p = 0.1 drops 26/256), and 0 < p < 1/512 rounds to
+    t = 0, i.e. no dropout (a warning says so)."""
+    p = float(dropout)
+    if 0.0 < p < 0.5 / 256:
+        warnings.warn(f"dropout rate {p} rounds to threshold 0 of 256: no element is dropped", stacklevel=3)
     return FaProblem(int(B), int(H), int(N), int(d), float(-1.0 if scale is None else scale),
-                     int(causal), int(in_dtype), int(H_kv), float(dropout), 0, int(seed) & (2 ** 64 - 1))
+                     int(causal), int(in_dtype), int(H_kv), p, 0, int(seed) & (2 ** 64 - 1))
 
 
 def tensor_arg(t) -> FaTensor:
@@ -168,13 +175,44 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _f32_like(x, out):
+def _keep_for_stream(stream, allocated):
+    """Tensors this binding allocated on torch's current stream but handed to
+    kernels on another stream: record that stream on them, so the caching
+    allocator does not reuse their memory before those kernels finish."""
+    torch = _torch()
+    if stream is None:
+        return
+    if isinstance(stream, int):
+        if stream == torch.cuda.current_stream().cuda_stream:
+            return
+        stream = torch.cuda.ExternalStream(stream)
+    elif stream.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in allocated:
+        t.record_stream(stream)
+
+
+def _f32_like(x, out, what):
+    """A float32 tensor shaped like x on x's device: ``out`` after checking
+    it, or a new one (second return value: whether it was allocated here)."""
     torch = _torch()
     if out is not None:
-        if out.dtype != torch.float32 or out.shape != x.shape:
-            raise ValueError("outputs must be float32 with the inputs' shape")
-        return out
-    return torch.empty(x.shape, dtype=torch.float32, device=x.device)
+        if out.dtype != torch.float32 or out.shape != x.shape or out.device != x.device:
+            raise ValueError(f"{what} must be float32 with shape {tuple(x.shape)} on {x.device}")
+        return out, False
+    return torch.empty(x.shape, dtype=torch.float32, device=x.device), True
+
+
+def _check_saved_state(q, o, lse):
+    """O from fa_fwd: float32, q's shape and device; L: a contiguous float32
+    [B, H, N] tensor on q's device (the library reads it by raw pointer)."""
+    torch = _torch()
+    B, H, N, _ = q.shape
+    if o.dtype != torch.float32 or o.shape != q.shape or o.device != q.device:
+        raise ValueError(f"o must be the float32 forward output with shape {tuple(q.shape)} on {q.device}")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or lse.device != q.device \
+            or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 tensor of shape {(B, H, N)} on {q.device}")
 
 
 def _call(name, status):
@@ -186,15 +224,22 @@ def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, causal=False, dro
     """Forward: returns (O fp32 [B,H,N,d], L fp32 [B,H,N], natural-log
     log-sum-exp of tau q.k over the (causally) valid keys).  k, v may have
     fewer heads than q (grouped-query / multi-query attention).  With
-    ``dropout`` > 0, O = (P * g) V for the keep mask g of (dropout, seed)."""
+    ``dropout`` > 0, O = (P * g) V for the keep mask g of (dropout, seed);
+    the rate is rounded to a multiple of 1/256 (see ``problem``)."""
     torch = _torch()
     B, H, N, d, Hkv = _check_inputs((q,), (k, v))
     p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
-    o = _f32_like(q, o)
+    o, new_o = _f32_like(q, o, "o")
+    allocated = [o] if new_o else []
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    _call("fa_fwd", load_library().fa_fwd(ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v),
-                                          tensor_arg(o), ctypes.c_void_p(lse.data_ptr()), _stream(stream)))
+        allocated.append(lse)
+    else:
+        _check_saved_state(q, o, lse)
+    lib = load_library()
+    _keep_for_stream(stream, allocated)
+    _call("fa_fwd", lib.fa_fwd(ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v),
+                               tensor_arg(o), ctypes.c_void_p(lse.data_ptr()), _stream(stream)))
     return o, lse
 
 
@@ -209,12 +254,16 @@ def bob_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False) -> int:
 
 
 def _workspace(nbytes, device, ws):
+    """A caller's workspace after checking it, or a new one (second return
+    value: whether it was allocated here)."""
     torch = _torch()
     if ws is None:
-        return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=device)
+        return torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=device), True
+    if ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"the workspace must be a contiguous tensor on {device}")
     if ws.numel() * ws.element_size() < nbytes:
-        raise ValueError("workspace too small")
-    return ws
+        raise ValueError(f"workspace too small: {ws.numel() * ws.element_size()} < {nbytes} bytes")
+    return ws, False
 
 
 def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None, stream=None,
@@ -223,10 +272,13 @@ def fa_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None, ws=None
     dK, dV have k's heads (sums over each group's query heads).  ``dropout``
     and ``seed`` must be the forward's."""
     B, H, N, d, Hkv = _check_inputs((q, dout), (k, v))
+    _check_saved_state(q, o, lse)
     p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
-    dq, dk, dv = _f32_like(q, dq), _f32_like(k, dk), _f32_like(k, dv)
+    outs = [_f32_like(q, dq, "dq"), _f32_like(k, dk, "dk"), _f32_like(k, dv, "dv")]
+    dq, dk, dv = (t for t, _ in outs)
     nbytes = int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
-    ws = _workspace(nbytes, q.device, ws)
+    ws, new_ws = _workspace(nbytes, q.device, ws)
+    _keep_for_stream(stream, [t for t, new in outs + [(ws, new_ws)] if new])
     _call("fa_bwd", load_library().fa_bwd(
         ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
         ctypes.c_void_p(lse.data_ptr()), tensor_arg(dout), tensor_arg(dq), tensor_arg(dk),
@@ -247,12 +299,14 @@ def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=N
     ``dropout`` and ``seed`` must be the forward's (the pages' analytical
     dropout extension)."""
     B, H, N, d, Hkv = _check_inputs((q, dout, uq), (k, v, uk, uv))
+    _check_saved_state(q, o, lse)
     p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
-    gq, gdo = _f32_like(q, gq), _f32_like(q, gdo)
-    gk, gv = _f32_like(k, gk), _f32_like(k, gv)
+    outs = [_f32_like(q, gq, "gq"), _f32_like(k, gk, "gk"), _f32_like(k, gv, "gv"), _f32_like(q, gdo, "gdo")]
+    gq, gk, gv, gdo = (t for t, _ in outs)
     lib = load_library()
     nbytes = int(lib.fa_bob_workspace_bytes(ctypes.byref(p)))
-    ws = _workspace(nbytes, q.device, ws)
+    ws, new_ws = _workspace(nbytes, q.device, ws)
+    _keep_for_stream(stream, [t for t, new in outs + [(ws, new_ws)] if new])
     args = [ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
             ctypes.c_void_p(lse.data_ptr()), tensor_arg(dout), tensor_arg(uq), tensor_arg(uk),
             tensor_arg(uv), tensor_arg(gq), tensor_arg(gk), tensor_arg(gv), tensor_arg(gdo),

@@ -108,7 +108,10 @@ def sdpa_bob(q, k, v, scale=None, causal=False, dropout_p=0.0, seed=0):
     (bf16 or fp32; k, v with H or a divisor of H heads), differentiable twice
     through the library's kernels.  Returns O in fp32.  ``scale`` defaults to
     1/sqrt(d).  ``dropout_p`` > 0 applies the library's dropout mask for
-    ``seed`` (O = (P * g) V); the same mask is used by both derivatives."""
+    ``seed`` (O = (P * g) V); the same mask is used by both derivatives.  The
+    rate is used as the nearest multiple of 1/256 (t = round(256 p) of 256
+    generator bytes drop an element, so p = 0.1 drops 26/256 = 10.16 %), and a
+    rate below 1/512 rounds to no dropout at all (the binding warns)."""
     for t in (q, k, v):
         if t.dim() != 4 or t.stride(-1) != 1:
             raise ValueError("q, k, v must be [B, H, N, d] with a contiguous head dimension")

@@ -65,7 +65,8 @@ typedef enum fa_status {
   FA_ERR_STRIDE = 3,      /* stride or alignment rule violated */
   FA_ERR_DTYPE = 4,       /* unknown input dtype */
   FA_ERR_UNSUPPORTED = 5, /* d not in {64, 128} (fp32 inputs: d = 64 only), causal not 0/1,
-                             a non-finite/negative scale, or a dropout rate outside [0, 255.5/256) */
+                             a NaN or +inf scale (any scale <= 0, -inf included, selects
+                             1/sqrt(d)), or a dropout rate outside [0, 255.5/256) */
   FA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required */
   FA_ERR_HIP = 7          /* the HIP runtime reported a launch error */
 } fa_status;

@@ -262,3 +262,41 @@ def test_three_pass_phases_in_order_equal_the_whole():
     for a_, b_ in zip(whole, outs + [ws]):
         n = a_.numel() if a_.dim() else 0
         assert bool((a_.flatten()[:n] == b_.flatten()[:n]).all())
+
+
+def test_binding_rejects_bad_arguments_before_launch():
+    """Wrongly typed, shaped or placed saved state, outputs and workspaces
+    raise ValueError in the binding, before the library is called; the
+    outputs given to the rejected calls are left untouched."""
+    import torch
+
+    import exact_second_order_fa_amd as fa
+
+    raw, _ = make_inputs(1, 2, 96, 64, 5, "bf16")
+    t = to_device(raw, "bf16")
+    q, k, v, do, uq, uk, uv = (t[n] for n in NAMES)
+    o, lse = fa.fa_fwd(q, k, v)
+    sentinel = torch.full(q.shape, 7.0, device="cuda")
+    good = dict(gq=sentinel)
+    bad_calls = {
+        "bf16 O": lambda: fa.fa_bob(q, k, v, o.to(torch.bfloat16), lse, do, uq, uk, uv, **good),
+        "O of another shape": lambda: fa.fa_bob(q, k, v, o[:, :1], lse, do, uq, uk, uv, **good),
+        "float64 L": lambda: fa.fa_bob(q, k, v, o, lse.double(), do, uq, uk, uv, **good),
+        "L of another length": lambda: fa.fa_bwd(q, k, v, o, lse[:, :, :50], do),
+        "strided L": lambda: fa.fa_bwd(q, k, v, o, torch.empty(1, 96, 2, device="cuda").permute(0, 2, 1), do),
+        "host L": lambda: fa.fa_bob(q, k, v, o, lse.cpu(), do, uq, uk, uv, **good),
+        "host O": lambda: fa.fa_bwd(q, k, v, o.cpu(), lse, do),
+        "host output": lambda: fa.fa_bob(q, k, v, o, lse, do, uq, uk, uv, gk=torch.empty(k.shape)),
+        "bf16 output": lambda: fa.fa_bwd(q, k, v, o, lse, do, dq=torch.empty(q.shape, dtype=torch.bfloat16,
+                                                                               device="cuda")),
+        "host workspace": lambda: fa.fa_bob(q, k, v, o, lse, do, uq, uk, uv, ws=torch.empty(1 << 20), **good),
+        "small workspace": lambda: fa.fa_bob(q, k, v, o, lse, do, uq, uk, uv,
+                                             ws=torch.empty(4, device="cuda"), **good),
+        "host fa_fwd lse": lambda: fa.fa_fwd(q, k, v, lse=torch.empty(1, 2, 96)),
+    }
+    for what, call in bad_calls.items():
+        with pytest.raises(ValueError):
+            call()
+        torch.cuda.synchronize()
+        say(f"  rejected: {what}")
+    assert bool((sentinel == 7.0).all())
