@@ -1,20 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of exact attention backward-over-backward (fa_bob) on one MI355X.
 
-A step is one fa_bob call: the row-scalar kernel (D = rowsum(dO * O)), the
-row-major pass and the column-major pass, on inputs already resident in HBM.
-fa_fwd (which supplies O and L) runs once before the timed region and is
-reported separately, as is fa_bwd.
+A step is one fa_bob call on inputs already resident in HBM: for bf16 inputs
+the row-major pass (which also computes D = rowsum(dO * O)) and the
+column-major pass; for fp32 inputs a row-scalar kernel runs first.  fa_fwd
+(which supplies O and L) runs once before the timed region and is reported
+separately, as is fa_bwd.
 
 Throughput: 38 B H N^2 d flops per step (19 N x N x d contractions per head:
-11 in the row pass, 8 in the column pass) divided by the step time, in
-TFLOP/s.  The default workload is "mid" (B=2, H=8, N=4096, d=64, bf16); the
-other bf16 workloads (N = 16K, 64K, 262K) are timed as a sweep in the same
-JSON line.
+11 in the row pass, 8 in the column pass; half for causal attention) divided
+by the step time, in TFLOP/s.  The default workload is "mid" (B=2, H=8,
+N=4096, d=64, bf16); the other workloads (N = 16K, 64K, 262K, the causal
+isolated-layer shapes and the multi-query range) are timed as a sweep in the
+same JSON line.
 
 Per-kernel times come from HIP events recorded on the launch stream between
-the three kernels of each timed step (fa_bob_phase 0, 1, 2 in order is
-exactly fa_bob).  The dominant kernel is the row pass (22 of the 38 flops).
+the kernels of each timed step (fa_bob_phase in order is exactly fa_bob).
+The dominant kernel is the row pass (22 of the 38 flops).  Progress lines go
+to stderr; the JSON line is the only line on stdout.
 """
 from __future__ import annotations
 
@@ -64,11 +67,49 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def host_info():
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process
+    may use, CPU model and RAM."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    ram = None
+    try:
+        ram = os.sysconf("SC_PAGE_SIZE") * os.sysconf("SC_PHYS_PAGES")
+    except (ValueError, OSError):
+        pass
+    return {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "cpu_model": model,
+            "ram_gib": round(ram / 2 ** 30, 1) if ram else None}
+
+
+# Workloads whose inputs are drawn on the device (torch's generator, same
+# distribution: N(0,1) rounded to bf16) because the host generator would
+# take minutes for them; they are timed, never compared with the oracle.
+DEVICE_DRAWN = ("gpt2c_64k", "gpt2c_256k")
+
+
 def device_inputs(w):
     import torch
 
-    from fa_inputs import workload_inputs
+    from fa_inputs import NAMES, workload_inputs
 
+    if w.name in DEVICE_DRAWN:
+        g = torch.Generator(device="cuda").manual_seed(w.seed)
+        out = {}
+        for n in NAMES:
+            heads = w.Hkv if n in ("k", "v", "uk", "uv") else w.H
+            out[n] = torch.randn((w.B, heads, w.N, w.d), device="cuda", generator=g).to(torch.bfloat16)
+        return out
     raw, _ = workload_inputs(w, with_f64=False)
     out = {}
     for k, v in raw.items():
@@ -135,15 +176,19 @@ def time_steps(r, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # bf16: phase 0 (the row-scalar kernel) launches nothing, D comes out of
+    # the row pass, so only phases 1 and 2 are timed.
+    phases = (1, 2) if r.w.dtype == "bf16" else (0, 1, 2)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(steps)]
     for s in range(steps):
         ev[s][0].record(stream)
-        for ph in range(3):
+        for i, ph in enumerate(phases):
             r.bob(phase=ph)
-            ev[s][ph + 1].record(stream)
+            ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
-    per = [float(np.mean([ev[s][ph].elapsed_time(ev[s][ph + 1]) for s in range(steps)])) for ph in range(3)]
-    step_ev = float(np.mean([ev[s][0].elapsed_time(ev[s][3]) for s in range(steps)]))
+    per = {ph: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)]))
+           for i, ph in enumerate(phases)}
+    step_ev = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps)]))
     return wall, step_ev, per
 
 
@@ -233,12 +278,12 @@ def traffic_for(workload):
 def cpu_baseline(w, heads):
     """The float64 oracle on a bounded sample (the first `heads` heads of the
     workload, full row and column passes), scaled to TFLOP/s in the same
-    38 N^2 d accounting."""
+    38 N^2 d accounting, on every CPU this process may use."""
     from fa_inputs import workload_inputs
     from oracle import col_pass, row_pass
 
     _, f64 = workload_inputs(w)
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = len(os.sched_getaffinity(0))
     done = 0
     t0 = time.perf_counter()
     for bh in range(heads):
@@ -251,7 +296,8 @@ def cpu_baseline(w, heads):
     flops = 38.0 * done * w.N * w.N * w.d
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} of {w.B * w.H} heads of workload {w.name} (N={w.N}, d={w.d}), full row and "
-                      f"column passes in float64, {dt:.1f} s"}
+                      f"column passes in float64 on a pool of {threads} threads, {dt:.1f} s",
+            "host": host_info()}
 
 
 def peak_of(w):
@@ -264,7 +310,8 @@ def streamed_bytes(w, schedule):
     pass streams K, V, U_K, U_V (8 d bytes per key per row block), the column
     pass Q, dO, U_Q and four row scalars (6 d + 16 bytes per row per key
     block), the three-pass alpha sweep K and U_K (4 d bytes per key per row
-    block).  Causal attention streams half."""
+    block).  Causal attention streams half.  Counted per query head (with
+    grouped heads, a key block streams the rows of the group's G heads)."""
     blocks = (w.N + 127) // 128
     row = blocks * w.N * 8 * w.d
     col = blocks * w.N * (6 * w.d + 16)
@@ -273,11 +320,51 @@ def streamed_bytes(w, schedule):
     return {"row_pass": row * f, "column_pass": col * f, "alpha_sweep": alpha * f, "total": (row + col + alpha) * f}
 
 
+def model_bytes(w):
+    """Algorithmic HBM bytes of one two-pass fa_bob call ([FlashBoB]
+    Theorem 4.3 with element sizes): the streamed tiles above plus the
+    stationary traffic, each resident block read once and each output written
+    once: Q, U_Q, dO (bf16) and O (fp32) and L by the row pass; K, V, U_K, U_V
+    (bf16) by the column pass; gQ, gdO, gK, gV written in fp32; D, alpha, E
+    and the four per-row chain inits (28 bytes per row) written by the row
+    pass."""
+    e = 2 if w.dtype == "bf16" else 4
+    qrows, krows = w.B * w.H * w.N, w.B * w.Hkv * w.N
+    stationary = qrows * (3 * e * w.d + 4 * w.d + 4) + krows * 4 * e * w.d
+    writes = qrows * (8 * w.d + 28) + krows * 8 * w.d
+    return {"stationary": stationary + writes, "streamed": streamed_bytes(w, 0)["total"],
+            "total": stationary + writes + streamed_bytes(w, 0)["total"]}
+
+
+def device_bytes(r):
+    """Device memory of one fa_bob call: what the workload holds resident
+    (inputs, O, L, outputs, workspace) and what the call itself adds (torch's
+    peak counter and the driver's free-memory delta; both 0: the library
+    allocates nothing and no N x N buffer exists)."""
+    import torch
+
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    r.bob()
+    torch.cuda.synchronize()
+    return {"resident": int(base), "call_peak_extra": int(torch.cuda.max_memory_allocated() - base),
+            "call_free_delta": int(free0 - torch.cuda.mem_get_info()[0])}
+
+
+def bob_flops_pass1(w):
+    """Row-pass flops: 11 of the 19 contractions, halved for causal attention."""
+    return 22.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+
+
 def ablation(names, reps=5):
     """Three-pass vs two-pass ([FlashBoB] appendix G.1) on the same kernel
     machinery: the two-pass row pass with one wave per SIMD (the kernel the
     three-pass row sweep is built from) against the three-pass schedule, and
-    the production two-pass (warp-specialised row pass) beside them."""
+    the production two-pass (warp-specialised row pass) beside them.  Calls
+    of a second or more are timed twice after one untimed call, with HIP
+    events between the phases of the same calls."""
     import torch
 
     from fa_inputs import WORKLOADS
@@ -285,18 +372,35 @@ def ablation(names, reps=5):
     out = {}
     for name in names:
         w = WORKLOADS[name]
+        progress(f"ablation {name}")
         r = Runner(w)
         res = {}
         for label, sched, nph in (("two_pass", 0, 3), ("two_pass_1wave", 1, 3), ("three_pass", 2, 4)):
-            n = reps_for(settle(lambda: r.bob(schedule=sched)), lo=reps)
-            ms = time_plain(lambda: r.bob(schedule=sched), n)
-            phases = [time_plain(lambda ph=ph: r.bob(phase=ph, schedule=sched), n) for ph in range(nph)]
+            t1 = settle(lambda: r.bob(schedule=sched))
+            if t1 < 500.0:
+                n = reps_for(t1, lo=reps)
+                ms = time_plain(lambda: r.bob(schedule=sched), n)
+                phases = [time_plain(lambda ph=ph: r.bob(phase=ph, schedule=sched), n) for ph in range(nph)]
+            else:
+                stream = torch.cuda.current_stream()
+                ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(2)]
+                for k in range(2):
+                    ev[k][0].record(stream)
+                    for ph in range(nph):
+                        r.bob(phase=ph, schedule=sched)
+                        ev[k][ph + 1].record(stream)
+                torch.cuda.synchronize()
+                phases = [float(np.mean([ev[k][ph].elapsed_time(ev[k][ph + 1]) for k in range(2)]))
+                          for ph in range(nph)]
+                ms = float(np.mean([ev[k][0].elapsed_time(ev[k][-1]) for k in range(2)]))
             res[label] = {"ms": round(ms, 3), "phase_ms": [round(x, 3) for x in phases]}
         sb2, sb3 = streamed_bytes(w, 0), streamed_bytes(w, 2)
         res["ratio_three_over_two_1wave"] = round(res["three_pass"]["ms"] / res["two_pass_1wave"]["ms"], 3)
         res["ratio_three_over_two"] = round(res["three_pass"]["ms"] / res["two_pass"]["ms"], 3)
         res["streamed_bytes"] = {"two_pass": sb2["total"], "three_pass": sb3["total"],
-                                 "saving_of_three_pass": round(1 - sb2["total"] / sb3["total"], 4)}
+                                 "saving_of_two_pass": round(1 - sb2["total"] / sb3["total"], 4)}
+        res["shape"] = {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                        "inputs": "drawn on the device" if name in DEVICE_DRAWN else "host generator"}
         if name in PAGES_ABLATION:
             res["pages_context"] = PAGES_ABLATION[name]
         out[name] = res
@@ -305,7 +409,35 @@ def ablation(names, reps=5):
     return out
 
 
+def sweep_leg(name):
+    import torch
+
+    from fa_inputs import WORKLOADS
+
+    sw = WORKLOADS[name]
+    progress(f"sweep {name}")
+    r = Runner(sw)
+    reps = reps_for(settle(r.bob))
+    _, s_ev, s_per = time_steps(r, reps, 0)
+    tf = sw.bob_flops / (s_ev * 1e9)
+    mb = model_bytes(sw)
+    res = {"B": sw.B, "H": sw.H, "H_kv": sw.Hkv, "N": sw.N, "d": sw.d, "causal": sw.causal,
+           "ms": round(s_ev, 3), "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+           "pass1_ms": round(s_per[1], 3), "pass2_ms": round(s_per[2], 3),
+           "model_GBps": round(mb["total"] / (s_ev * 1e6), 1),
+           "device_bytes": device_bytes(r)}
+    if 0 in s_per:
+        res["rowscalar_ms"] = round(s_per[0], 4)
+    if name in PAGES_MS:
+        res["pages_ms_context"] = PAGES_MS[name]
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
+    from fa_inputs import MQA_SWEEP
+
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # Defaults: 200 warm-up steps (about 130 ms on the mid workload) take the
@@ -313,9 +445,9 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="mid")
-    ap.add_argument("--sweep", default="hd128,long,max,gpt2c_4k,gpt2c_16k,c128_16k,mqa_32k",
+    ap.add_argument("--sweep", default="hd128,long,max,gpt2c_4k,gpt2c_16k,c128_16k," + ",".join(MQA_SWEEP),
                     help="comma list of extra workloads ('' for none)")
-    ap.add_argument("--ablation", default="gpt2c_4k,gpt2c_16k",
+    ap.add_argument("--ablation", default="gpt2c_4k,gpt2c_16k,gpt2c_64k,gpt2c_256k",
                     help="workloads of the three-pass vs two-pass schedule ablation ('' for none)")
     ap.add_argument("--only-ablation", action="store_true", help="run only the schedule ablation (profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -352,11 +484,20 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    progress(f"workload {w.name}: inputs")
     r = Runner(w)
-    wall, step_ev, per = time_steps(r, args.steps, args.warmup)
-    bob_ms = time_plain(r.bob, args.steps)
+    # Legs on the same resident inputs first (one Hessian-vector product
+    # through sdpa_bob; fa_fwd and fa_bwd), then the headline: W warm-up and K
+    # timed fa_bob steps, which so start at the clock those legs leave.
+    progress("hvp step")
+    hvp = hvp_leg(r)
+    progress("prerequisites")
     fwd_ms = time_plain(r.fwd, max(3, args.steps // 4))
     bwd_ms = time_plain(r.bwd, max(3, args.steps // 4))
+    progress(f"headline: {args.warmup} warm-up and {args.steps} timed steps")
+    wall, step_ev, per = time_steps(r, args.steps, args.warmup)
+    bob_ms = time_plain(r.bob, args.steps)
+    dev_bytes = device_bytes(r)
     # Prerequisites ([FlashBoB] section 3): 2 N^2 d flops per contraction;
     # forward 2 contractions, first backward 5 (S, dP, dV, dQ, dK); causal half.
     cf = (0.5 if w.causal else 1.0) * 2.0 * w.B * w.H * w.N * w.N * w.d
@@ -365,29 +506,19 @@ def main():
               "fa_bwd": {"ms": round(bwd_ms, 4), "tflops": round(5 * cf / (bwd_ms * 1e9), 1),
                          "frac_peak": round(5 * cf / (bwd_ms * 1e9) / peak_of(w), 4)}}
     flops = w.bob_flops
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    peak = peak_of(w)
     value = flops / (wall * 1e9)
-    pass1_flops = 22.0 * w.B * w.H * w.N * w.N * w.d
+    pass1_flops = bob_flops_pass1(w)
     ach = pass1_flops / (per[1] * 1e9)
     traffic = traffic_for(w.name)
-    hvp = hvp_leg(r)
+    mb = model_bytes(w)
 
     sweep = {}
-    for name in [s for s in args.sweep.split(",") if s]:
-        sw = WORKLOADS[name]
+    for name in [s_ for s_ in args.sweep.split(",") if s_]:
         del r
         torch.cuda.empty_cache()
-        r = Runner(sw)
-        reps = reps_for(settle(r.bob))
-        _, s_ev, s_per = time_steps(r, reps, 0)
-        tf = sw.bob_flops / (s_ev * 1e9)
-        sweep[name] = {"B": sw.B, "H": sw.H, "H_kv": sw.Hkv, "N": sw.N, "d": sw.d, "causal": sw.causal,
-                       "ms": round(s_ev, 3),
-                       "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                       "pass1_ms": round(s_per[1], 3), "pass2_ms": round(s_per[2], 3),
-                       "rowscalar_ms": round(s_per[0], 4)}
-        if name in PAGES_MS:
-            sweep[name]["pages_ms_context"] = PAGES_MS[name]
+        r = None
+        sweep[name] = sweep_leg(name)
 
     # The dropout variant ([FlashBoB] appendix G) on the same workload, with
     # the Philox mask, reported beside the headline.
@@ -395,13 +526,21 @@ def main():
     if args.dropout > 0:
         del r
         torch.cuda.empty_cache()
+        progress("dropout variant")
         r = Runner(w, dropout=args.dropout, seed=1234)
         d_ms = time_plain(r.bob, reps_for(settle(r.bob)))
-        dropout_leg = {"p": args.dropout, "workload": w.name, "fa_bob_ms": round(d_ms, 4),
+        dropout_leg = {"p": args.dropout, "seed": 1234, "workload": w.name, "fa_bob_ms": round(d_ms, 4),
                        "tflops": round(w.bob_flops / (d_ms * 1e9), 1),
+                       "ratio_to_dropout_free": round(d_ms / bob_ms, 3),
                        "kernels": ("LDS-DMA row pass and split-schedule column pass" if w.dtype == "bf16"
                                    else "portable") + ", mask from Philox4x64-10"}
 
+    kernels_ms = {"bob_pass1": round(per[1], 4), "bob_pass2": round(per[2], 4), "step_events": round(step_ev, 4),
+                  "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)}
+    if 0 in per:
+        kernels_ms["rowscalar"] = round(per[0], 4)
+    else:
+        kernels_ms["row_scalars"] = "D = rowsum(dO * O) is computed inside bob_pass1 (no separate kernel)"
     line = {
         "metric": "fa_bob TFLOP/s (38 B H N^2 d flops per call) and fraction of bf16 dense MFMA peak",
         "value": round(value, 2),
@@ -421,9 +560,11 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "bob_pass1 (row pass)", "achieved": round(ach, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                      "traffic": traffic, "flops_per_launch": pass1_flops},
-        "kernels_ms": {"rowscalar": round(per[0], 4), "bob_pass1": round(per[1], 4),
-                       "bob_pass2": round(per[2], 4), "step_events": round(step_ev, 4),
-                       "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)},
+        "hbm": {"model_bytes_per_call": mb, "model_GBps": round(mb["total"] / (wall * 1e6), 1),
+                "pass1_counter_GBps": (round(traffic / (per[1] * 1e6), 1) if traffic else None),
+                "peak_GBps": 8000.0},
+        "device_bytes": dev_bytes,
+        "kernels_ms": kernels_ms,
         "prerequisites": prereq,
         "sweep": sweep,
         "dropout_variant": dropout_leg,
@@ -432,8 +573,10 @@ def main():
     if abl_names:
         del r
         torch.cuda.empty_cache()
+        r = None
         line["schedule_ablation"] = ablation(abl_names)
     if not args.no_cpu:
+        progress("CPU baseline")
         nh = w.B * w.H if args.cpu_heads <= 0 else min(args.cpu_heads, w.B * w.H)
         line["cpu_baseline"] = cpu_baseline(w, nh)
     print(json.dumps(line), flush=True)
