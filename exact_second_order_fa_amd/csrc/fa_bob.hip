@@ -57,6 +57,12 @@ __device__ inline f32x16 mfma_first_w(bf16x8 a, bf16x8 b) {
 __device__ inline void mfma_v_w(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+// d = a * b (C = 0) with b resident in AGPRs.
+__device__ inline f32x16 mfma_first_a(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
+  return d;
+}
 // d += a * b, d in VGPRs, b resident in AGPRs.
 __device__ inline void mfma_va(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(b));
@@ -672,9 +678,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           if (t * TS + sub * 32 + acc_pos(idx, hh) < col) s[idx] = -INFINITY;
         asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
       }
-      dp = DROP ? zero16() : row_init<TS>(sc + TS, sub);
+      // With DROP the dP and C chains start at 0: their first MFMA takes the
+      // literal 0 as C, so no zero-filled registers (which the compiler
+      // would copy in with a VALU write right before the MFMA) are read.
+      if constexpr (!DROP) {
+        dp = row_init<TS>(sc + TS, sub);
+        c = row_init<TS>(sc + 3 * TS, sub);
+      }
       f = row_init<TS>(sc + 2 * TS, sub);
-      c = DROP ? zero16() : row_init<TS>(sc + 3 * TS, sub);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bf16x8 xq = rd_row<D, TS>(tq, rd, sub, ks);
@@ -683,7 +694,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mfma_v(s, xq, kf[ks]);
         mfma_v(f, xuq, kf[ks]);
         mfma_v(f, xq, ukf[ks]);
-        if constexpr (RESA) {
+        if (DROP && ks == 0) {
+          dp = RESA ? mfma_first_a(xd, vf[0]) : mfma_first(xd, vf[0]);
+          c = RESA ? mfma_first_a(xd, uvf[0]) : mfma_first(xd, uvf[0]);
+        } else if constexpr (RESA) {
           mfma_va(dp, xd, vf[ks]);
           mfma_va(c, xd, uvf[ks]);
         } else {

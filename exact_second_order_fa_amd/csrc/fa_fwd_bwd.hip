@@ -26,12 +26,6 @@ __device__ inline void mfma_vacc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ inline void vfence1(f32x16& a) { asm volatile("s_nop 7\n\ts_nop 4" : "+v"(a)); }
-// d = a * b (C = 0) with b resident in AGPRs.
-__device__ inline f32x16 mfma_first_a(bf16x8 a, bf16x8 b) {
-  f32x16 d;
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(b));
-  return d;
-}
 
 // ---------------------------------------------------------------------------
 // Forward: O = softmax(tau Q K^T) V with the online softmax, L = log-sum-exp.

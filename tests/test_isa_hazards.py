@@ -8,7 +8,7 @@ import subprocess
 import pytest
 
 from exact_second_order_fa_amd import build
-from tests.isa_hazards import check_asm, check_kernel
+from tests.isa_hazards import check_asm, check_kernel, check_loops
 
 
 def test_checker_flags_planted_hazards():
@@ -20,11 +20,41 @@ def test_checker_flags_planted_hazards():
     assert any(e.startswith("R2") for e in check_kernel(bad))
     bad2 = ["v_mov_b32_e32 v16, 0", "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0"]
     assert any(e.startswith("R1") for e in check_kernel(bad2))
+    # One wait state is one too few: an operand reloaded from an AGPR with a
+    # single instruction before the MFMA (the two-waves-per-SIMD dK/dV
+    # dropout kernel's wrong dK), and a zero-filled C copied in the same way.
+    bad3 = ["v_accvgpr_read_b32 v23, a95", "s_waitcnt lgkmcnt(0)",
+            "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"]
+    assert any(e.startswith("R1") for e in check_kernel(bad3))
+    bad4 = ["v_mov_b64_e32 v[0:1], v[32:33]", "s_waitcnt lgkmcnt(0)",
+            "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"]
+    assert any(e.startswith("R1") for e in check_kernel(bad4))
+    assert check_kernel(["v_accvgpr_read_b32 v23, a95", "s_nop 1",
+                         "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], v[0:15]"]) == []
     good = ["v_mov_b32_e32 v16, 0", "s_nop 1",
             "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]",
             "v_mfma_f32_32x32x16_bf16 a[0:15], v[16:19], v[20:23], a[0:15]",
             "s_nop 7", "s_nop 3", "v_accvgpr_read_b32 v30, a3"]
     assert check_kernel(good) == []
+
+
+def test_checker_flags_planted_dma_and_back_edge_hazards():
+    """R5: a spilled SGPR read back by v_readlane and used at once as the base
+    of an LDS-DMA load; R6: M0 written right before the load; a hazard that
+    only exists from the end of a loop body to its start."""
+    bad5 = ["v_readlane_b32 s4, v127, 2", "s_mov_b32 m0, s8", "s_nop 0",
+            "global_load_lds_dwordx4 v4, s[4:5]"]
+    assert any(e.startswith("R5") for e in check_kernel(bad5))
+    good5 = ["v_readlane_b32 s4, v127, 2", "s_nop 3", "s_mov_b32 m0, s8", "s_nop 0",
+             "global_load_lds_dwordx4 v4, s[4:5]"]
+    assert check_kernel(good5) == []
+    bad6 = ["s_mov_b32 m0, s8", "global_load_lds_dwordx4 v4, s[4:5]"]
+    assert any(e.startswith("R6") for e in check_kernel(bad6))
+    loop = [".LBB0_1:", "v_add_f32_e32 v0, v1, v2",
+            "v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0",
+            "s_cbranch_scc1 .LBB0_1"]
+    assert check_kernel(loop) == []           # straight-line: no reader after the MFMA
+    assert any(e.startswith("R2") for e in check_loops(loop))  # next iteration's VALU writes v0
 
 
 @pytest.mark.skipif(not (shutil.which("hipcc") or os.path.exists("/opt/rocm/bin/hipcc")), reason="hipcc missing")
