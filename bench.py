@@ -136,7 +136,7 @@ class Runner:
         self.o, self.lse = fa.fa_fwd(self.t["q"], self.t["k"], self.t["v"], causal=w.causal, **self.drop)
         self.outs = [torch.empty(s, dtype=torch.float32, device="cuda") for s in (shape, kshape, kshape, shape)]
         code = fa.FA_BF16 if w.dtype == "bf16" else fa.FA_FP32
-        self.ws = torch.empty(fa.bob_workspace_bytes(*shape, code, w.causal) // 4, dtype=torch.float32,
+        self.ws = torch.empty(fa.bob_workspace_bytes(*shape, code, w.causal, w.Hkv) // 4, dtype=torch.float32,
                               device="cuda")
         torch.cuda.synchronize()
 

@@ -243,13 +243,15 @@ def fa_fwd(q, k, v, scale=None, o=None, lse=None, stream=None, causal=False, dro
     return o, lse
 
 
-def bwd_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False) -> int:
-    p = problem(B, H, N, d, in_dtype, None, int(bool(causal)))
+def bwd_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False, H_kv=0) -> int:
+    p = problem(B, H, N, d, in_dtype, None, int(bool(causal)), H_kv)
     return int(load_library().fa_bwd_workspace_bytes(ctypes.byref(p)))
 
 
-def bob_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False) -> int:
-    p = problem(B, H, N, d, in_dtype, None, int(bool(causal)))
+def bob_workspace_bytes(B, H, N, d, in_dtype=FA_BF16, causal=False, H_kv=0) -> int:
+    """Bytes of fa_bob's workspace (it depends on H_kv: grouped-query
+    problems with few key blocks also hold the column pass's partial sums)."""
+    p = problem(B, H, N, d, in_dtype, None, int(bool(causal)), H_kv)
     return int(load_library().fa_bob_workspace_bytes(ctypes.byref(p)))
 
 

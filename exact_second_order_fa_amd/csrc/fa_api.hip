@@ -114,6 +114,9 @@ Args base_args(const Ctx& c) {
   a.H = (int)c.H;
   a.Hk = (int)c.Hkv;
   a.G = (int)c.G;
+  a.gs = (int)c.G;
+  a.nsplit = 1;
+  a.part = nullptr;
   a.N = (int)c.N;
   a.tau = c.tau;
   a.pow2 = c.pow2;
@@ -137,6 +140,46 @@ unsigned grid_cols(const Ctx& c) {
 
 // Rows per head padded to whole 128-row blocks (the staged chain-init layout).
 int64_t padded_rows(const Ctx& c) { return (c.N + fa::kPsRows - 1) / fa::kPsRows * fa::kPsRows; }
+
+// Group split of the bf16 column kernels.  A column workgroup streams the
+// rows of its key/value head's G query heads, so grouped-query attention
+// with few key blocks launches few workgroups (multi-query at N = 2048: 16
+// for 256 CUs).  Then each key block's G query heads are split over nsplit
+// workgroups (the smallest divisor of G that gives one per CU, else G), each
+// leaving its sums in the workspace, and a sum kernel adds the nsplit
+// partial results in a fixed order and writes each output block once.
+int group_split(const Ctx& c) {
+  if (!c.bf || c.G == 1) return 1;
+  const int64_t cols = c.B * c.Hkv * ((c.N + fa::kResRows - 1) / fa::kResRows);
+  if (cols >= 256) return 1;
+  for (int s = 2; s < c.G; ++s)
+    if (c.G % s == 0 && cols * s >= 256) return s;
+  return (int)c.G;
+}
+
+// Floats of the partial key-side sums of a group split: [2][nsplit][B * H_kv][N][d].
+size_t split_floats(const Ctx& c, int nsplit) {
+  return nsplit > 1 ? 2 * (size_t)nsplit * (size_t)(c.B * c.Hkv * c.N) * (size_t)c.d : 0;
+}
+
+// Workspace offsets in floats: fa_bob [D | alpha | E | chain inits | partial
+// sums], fa_bwd [D | chain inits | partial sums]; the partial sums start on a
+// 256-byte boundary.
+size_t align64(size_t f) { return (f + 63) / 64 * 64; }
+size_t bob_part_offset(const Ctx& c) {
+  return align64(3 * (size_t)(c.B * c.H * c.N) + 4 * (size_t)(c.B * c.H) * (size_t)padded_rows(c));
+}
+size_t bwd_part_offset(const Ctx& c) {
+  return align64((size_t)(c.B * c.H * c.N) + 2 * (size_t)(c.B * c.H) * (size_t)padded_rows(c));
+}
+
+// Launch of the partial-sum kernel after a split column kernel.
+template <int D>
+void launch_group_sum(const Ctx& c, const fa::Args& a, hipStream_t st) {
+  if (a.nsplit <= 1) return;
+  const int64_t threads = 2 * (int64_t)(c.B * c.Hkv * c.N) * (D / 4);
+  hipLaunchKernelGGL((fa::group_sum_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
+}
 
 // staged: the launch also covers each head's padding rows (fa_bwd's column
 // chain inits).
@@ -201,14 +244,15 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
     // Row scalars D plus the staged chain inits (-L/rho, -D) of the column kernel.
     hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c, true)), dim3(256), 0, st, a);
     constexpr int TS = D == 64 ? 128 : 64;
+    const dim3 gc(grid_cols(c) * a.nsplit);
     if (c.drop) {
       hipLaunchKernelGGL((fa::bwd_dq_dma_kernel<D, TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
-      hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C, true>), dim3(grid_cols(c)), dim3(fa::kThreads), 0, st,
-                         a);
+      hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C, true>), gc, dim3(fa::kThreads), 0, st, a);
     } else {
       hipLaunchKernelGGL((fa::bwd_dq_dma_kernel<D, TS, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
-      hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C>), dim3(grid_cols(c)), dim3(fa::kThreads), 0, st, a);
+      hipLaunchKernelGGL((fa::bwd_dkdv_dma_kernel<D, TS, C>), gc, dim3(fa::kThreads), 0, st, a);
     }
+    launch_group_sum<D>(c, a, st);
   } else {
     Args b = a;
     b.bs = nullptr;
@@ -229,7 +273,7 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
 // phase < 0 runs the whole schedule; otherwise only that kernel.
 template <typename T, int D, bool RHO1, bool C>
 void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int phase) {
-  const dim3 g(grid_rows(c)), b(fa::kThreads), gc(grid_cols(c));
+  const dim3 g(grid_rows(c)), b(fa::kThreads), gc(grid_cols(c) * a.nsplit);
   auto want = [&](int ph) { return phase < 0 || phase == ph; };
   if (c.drop) {  // two-pass schedule (schedule 2 is refused earlier)
     if constexpr (sizeof(T) == 2) {
@@ -246,6 +290,7 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
           hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, true, false, C, true>), gc, b, 0, st, a);
         else
           hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C, true>), gc, b, 0, st, a);
+        launch_group_sum<D>(c, a, st);
       }
     } else {
       if (want(0)) launch_rowscalar<T, D>(c, a, st);
@@ -286,6 +331,7 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
         hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), gc, b, 0, st, a);
       else
         hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), gc, b, 0, st, a);
+      launch_group_sum<D>(c, a, st);
     }
   } else {
     if (want(1)) hipLaunchKernelGGL((fa::bob_pass1_kernel<T, D, Tiles<T, D>::TS, RHO1, C>), g, b, 0, st, a);
@@ -349,14 +395,13 @@ const char* fa_status_str(fa_status s) {
 size_t fa_bwd_workspace_bytes(const fa_problem* p) {
   Ctx c;
   if (check_problem(p, &c) != FA_OK) return 0;
-  return ((size_t)(c.B * c.H * c.N) + 2 * (size_t)(c.B * c.H) * (size_t)padded_rows(c)) * sizeof(float);
+  return (bwd_part_offset(c) + split_floats(c, group_split(c))) * sizeof(float);
 }
 
 size_t fa_bob_workspace_bytes(const fa_problem* p) {
   Ctx c;
   if (check_problem(p, &c) != FA_OK) return 0;
-  const size_t padded = (size_t)((c.N + fa::kPsRows - 1) / fa::kPsRows) * fa::kPsRows;
-  return (3 * (size_t)(c.B * c.H * c.N) + 4 * (size_t)(c.B * c.H) * padded) * sizeof(float);
+  return (bob_part_offset(c) + split_floats(c, group_split(c))) * sizeof(float);
 }
 
 fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
@@ -408,6 +453,9 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
   a.lse = lse;
   a.D = reinterpret_cast<float*>(workspace);
   a.bs = a.D + (size_t)(c.B * c.H * c.N);
+  a.nsplit = group_split(c);
+  a.gs = (int)(c.G / a.nsplit);
+  a.part = a.nsplit > 1 ? a.D + bwd_part_offset(c) : nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   dispatch3<BwdL>(c, a, st);
@@ -457,6 +505,9 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   a.alpha = a.D + nrow;
   a.E = a.D + 2 * nrow;
   a.ps = a.D + 3 * nrow;
+  a.nsplit = group_split(c);
+  a.gs = (int)(c.G / a.nsplit);
+  a.part = a.nsplit > 1 ? a.D + bob_part_offset(c) : nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   dispatch3<BobL>(c, a, st, schedule, phase);

@@ -418,14 +418,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   int u = 0;  // tiles of all heads so far (picks the LDS buffer)
-  for (int g = 0; g < a.G; ++g) {
+  for (int g = 0; g < a.gs; ++g) {
     auto run = [&](int t0, int t1, auto mode_c) {
       for (int t = t0; t < t1; ++t) {
         dma_wait();
         __syncthreads();
         const bool wrap = t + 1 >= nt;
         const int gn = wrap ? g + 1 : g, tn = wrap ? t_begin : t + 1;
-        if (gn < a.G) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
+        if (gn < a.gs) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
         tile_body(t, u & 1, g, mode_c);
         ++u;
       }
@@ -435,12 +435,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     run(CAUSAL ? min(t_diag, nt) : 0, nt, std::integral_constant<int, 0>{});
   }
   acc_fence2<NDB>(ak, av);
-  float* dk = head_out(a.r1, wk.b, wk.hk);
-  float* dv = head_out(a.r2, wk.b, wk.hk);
+  const KeyOut out = key_out<D>(a, wk);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
-    store_out(dk, a.r1.sn, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
-    store_out(dv, a.r2.sn, col, N, db, [&](int idx) { return av[db][idx]; });
+    store_out(out.k, out.sk, col, N, db, [&](int idx) { return a.tau * ak[db][idx]; });
+    store_out(out.v, out.sv, col, N, db, [&](int idx) { return av[db][idx]; });
   }
 }
 

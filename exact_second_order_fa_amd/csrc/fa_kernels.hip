@@ -35,8 +35,10 @@ struct Args {
   float* E;                            // [B,H,N] BoB row scalar E
   float* ps;                           // [B*H][ceil(N/128)][4][128] column-pass chain inits
   float* bs;                           // [B*H][ceil(N/128)][2][128] first-backward column chain inits (or null)
+  float* part;                         // key-side partial sums of a split group (or null), see GroupSplit
   int B, H, N;
   int Hk, G;                 // key/value heads and query heads per key/value head (H = Hk * G)
+  int gs, nsplit;            // column kernels: query heads per workgroup (G / nsplit) and splits of a group
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
   uint64_t seed;             // dropout: generator key
   uint32_t drop_thr;         // dropout: keep an element iff its byte >= drop_thr (1..255)
@@ -64,6 +66,7 @@ __device__ inline float* head_out(const TDesc& t, int b, int h) {
 //     over the group inside one workgroup).
 struct Work {
   int bh, b, h, hk, rb;
+  int sp;  // column kernels: which split of the group's query heads (0 without a split)
 };
 
 // heavy_first: causal row-side kernels do work proportional to rb + 1; the
@@ -81,16 +84,72 @@ __device__ inline Work work_item(const Args& a, bool heavy_first = false) {
   return r;
 }
 
+// With a group split (nsplit > 1: few key blocks, many query heads per
+// key/value head) workgroup sp of a key block takes query heads
+// hk * G + sp * gs .. + gs - 1 and leaves its sums in a.part; the split index
+// is the slowest, so the workgroups streaming the same query heads sit on one
+// XCD.
 __device__ inline Work work_item_cols(const Args& a) {
   const int nblk = (a.N + kResRows - 1) / kResRows;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = a.B * a.Hk * nblk;
   Work r;
-  r.bh = w / nblk;
-  r.rb = w % nblk;
+  r.sp = w / per;
+  const int w2 = w - r.sp * per;
+  r.bh = w2 / nblk;
+  r.rb = w2 % nblk;
   r.b = r.bh / a.Hk;
   r.hk = r.bh % a.Hk;
-  r.h = r.hk * a.G;
+  r.h = r.hk * a.G + r.sp * a.gs;
   return r;
+}
+
+// Key-side output rows of a column workgroup: the caller's tensor, or with a
+// group split this split's slab of a.part ([2][nsplit][B * Hk][N][D] floats:
+// first the d~K sums, then the d~V sums).
+struct KeyOut {
+  float* k;
+  float* v;
+  int64_t sk, sv;
+};
+template <int D>
+__device__ inline KeyOut key_out(const Args& a, const Work& wk) {
+  KeyOut o;
+  if (a.part) {
+    const int64_t slab = (int64_t)a.B * a.Hk * a.N * D;
+    o.k = a.part + ((int64_t)wk.sp * a.B * a.Hk + wk.bh) * a.N * D;
+    o.v = o.k + a.nsplit * slab;
+    o.sk = o.sv = D;
+  } else {
+    o.k = head_out(a.r1, wk.b, wk.hk);
+    o.v = head_out(a.r2, wk.b, wk.hk);
+    o.sk = a.r1.sn;
+    o.sv = a.r2.sn;
+  }
+  return o;
+}
+
+// Sum of the nsplit partial key-side outputs, in split order (deterministic),
+// into the caller's tensors: one thread per 4 consecutive floats of a row.
+template <int D>
+__global__ __launch_bounds__(256) void group_sum_kernel(Args a) {
+  const int64_t rows = (int64_t)a.B * a.Hk * a.N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * rows * (D / 4)) return;
+  const int which = (int)(i / (rows * (D / 4)));  // 0: d~K, 1: d~V
+  const int64_t j = i - (int64_t)which * rows * (D / 4);
+  const int64_t row = j / (D / 4);
+  const int c = (int)(j % (D / 4)) * 4;
+  const int64_t slab = rows * D;
+  const float* src = a.part + (int64_t)which * a.nsplit * slab + row * D + c;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int sp = 1; sp < a.nsplit; ++sp) acc += *reinterpret_cast<const f32x4*>(src + sp * slab);
+  const int b = (int)(row / ((int64_t)a.Hk * a.N));
+  const int hk = (int)(row / a.N % a.Hk);
+  const int n = (int)(row % a.N);
+  const TDesc& t = which ? a.r2 : a.r1;
+  float* dst = head_out(t, b, hk) + (int64_t)n * t.sn + c;
+  *reinterpret_cast<f32x4*>(dst) = acc;
 }
 
 // Row scalars of a streamed tile, staged into LDS next to the operand tiles.

@@ -73,15 +73,35 @@ def test_problem_struct_layout(tmp_path):
                    FaProblem.H_kv.offset, FaProblem.dropout.offset, FaProblem.seed.offset, ctypes.sizeof(FaTensor)]
 
 
+def _align64(f):
+    return (f + 63) // 64 * 64
+
+
 def test_workspace_sizes(lib):
     p = prob(2, 3, 130, 64)
-    # grouped-query attention does not change the workspace (all per query head)
-    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, Hkv=1))) == \
-        lib.fa_bob_workspace_bytes(ctypes.byref(p))
     # D, alpha, E ([B,H,N] fp32 each), then four chain inits per row padded to 128 rows
-    assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == (3 * 2 * 3 * 130 + 4 * 2 * 3 * 256) * 4
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(p)) == _align64(3 * 2 * 3 * 130 + 4 * 2 * 3 * 256) * 4
     # D ([B,H,N] fp32), then two chain inits per row padded to 128 rows
-    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == (2 * 3 * 130 + 2 * 2 * 3 * 256) * 4
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(p)) == _align64(2 * 3 * 130 + 2 * 2 * 3 * 256) * 4
+    # Grouped-query attention with few key blocks splits each key block's
+    # query heads over several workgroups, whose partial key-side sums
+    # ([2][nsplit][B*H_kv][N][d] fp32) follow: 2 x 1 key/value heads x 2 key
+    # blocks = 4 column workgroups, so the group of 3 is split 3 ways.
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, Hkv=1))) == \
+        (_align64(3 * 2 * 3 * 130 + 4 * 2 * 3 * 256) + 2 * 3 * 2 * 1 * 130 * 64) * 4
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, Hkv=1))) == \
+        (_align64(2 * 3 * 130 + 2 * 2 * 3 * 256) + 2 * 3 * 2 * 1 * 130 * 64) * 4
+    # Enough key blocks (B * H_kv * ceil(N/128) >= 256): no split, nothing extra.
+    big = prob(1, 8, 32768, 64, Hkv=1)
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(big)) == _align64(3 * 8 * 32768 + 4 * 8 * 32768) * 4
+    # The smallest divisor of G that reaches 256 workgroups: 1 x 1 x 64 key
+    # blocks at N = 8192, G = 8 -> 4 splits.
+    mid = prob(1, 8, 8192, 64, Hkv=1)
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(mid)) == \
+        (_align64(3 * 8 * 8192 + 4 * 8 * 8192) + 2 * 4 * 8192 * 64) * 4
+    # fp32 inputs run the portable kernels, which never split.
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, Hkv=1, dt=fa.FA_FP32))) == \
+        lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, dt=fa.FA_FP32)))
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(d=96))) == 0
     assert lib.fa_bob_workspace_bytes(None) == 0
 
@@ -212,3 +232,4 @@ def test_schedule_checks_tensors_too(lib):
     bad = [t() for _ in range(12)]
     bad[0] = t(ptr=0)
     assert sched(lib, prob(), 2, -1, bad) == 1
+

@@ -259,9 +259,9 @@ def test_three_pass_phases_in_order_equal_the_whole():
     for ph in range(4):
         fa.fa_bob(*args, gq=outs[0], gk=outs[1], gv=outs[2], gdo=outs[3], ws=ws, schedule=THREE, phase=ph)
     torch.cuda.synchronize()
-    for a_, b_ in zip(whole, outs + [ws]):
-        n = a_.numel() if a_.dim() else 0
-        assert bool((a_.flatten()[:n] == b_.flatten()[:n]).all())
+    # the outputs and the workspace's D, alpha, E (its ABI part)
+    for a_, b_ in zip(whole[:4] + (whole[4][:3 * 2 * 333],), outs + [ws[:3 * 2 * 333]]):
+        assert bool((a_ == b_).all())
 
 
 def test_binding_rejects_bad_arguments_before_launch():
