@@ -19,9 +19,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_OK = 0
-# fa_version() the binding needs: 1.1 added fa_problem.H_kv; an older library
-# would read key-side tensors with the query-head count.
-MIN_VERSION = 10200
+# fa_version() the binding needs: 1.1 added fa_problem.H_kv (an older library
+# would read key-side tensors with the query-head count), 1.3 fa_bob_noalloc.
+MIN_VERSION = 10300
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_STRIDE", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_UNSUPPORTED", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP",
@@ -30,7 +30,9 @@ FA_BF16, FA_FP32 = 0, 1
 
 # Exported symbols (kept equal to the declarations in include/fa.h).
 SYMBOLS = ("fa_version", "fa_status_str", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
-           "fa_bob_workspace_bytes", "fa_bob", "fa_bob_phase", "fa_bob_schedule")
+           "fa_bob_workspace_bytes", "fa_bob", "fa_bob_noalloc", "fa_bob_phase", "fa_bob_schedule")
+# Size of fa_bob_noalloc's static device workspace (FA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 # Schedules of fa_bob_schedule (include/fa.h).
 SCHED_TWO_PASS, SCHED_TWO_PASS_1WAVE, SCHED_THREE_PASS = 0, 1, 2
 
@@ -86,6 +88,8 @@ def load_library(path: str | None = None, check_version: bool = True) -> ctypes.
     lib.fa_bwd.argtypes = [P, T, T, T, T, vp, T, T, T, T, vp, sz, vp]
     lib.fa_bob.restype = ctypes.c_int
     lib.fa_bob.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, vp]
+    lib.fa_bob_noalloc.restype = ctypes.c_int
+    lib.fa_bob_noalloc.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp]
     lib.fa_bob_phase.restype = ctypes.c_int
     lib.fa_bob_phase.argtypes = [P, T, T, T, T, vp, T, T, T, T, T, T, T, T, vp, sz, ctypes.c_int32, vp]
     lib.fa_bob_schedule.restype = ctypes.c_int
@@ -322,6 +326,28 @@ def fa_bob(q, k, v, o, lse, dout, uq, uk, uv, scale=None, gq=None, gk=None, gv=N
     else:
         _call("fa_bob_phase", lib.fa_bob_phase(*args, ctypes.c_int32(phase), _stream(stream)))
     return gq, gk, gv, gdo, ws
+
+
+def fa_bob_noalloc(q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, scale=None, stream=None, causal=False,
+                   dropout=0.0, seed=0):
+    """fa_bob without a workspace, for callers that must not allocate device
+    memory: the library keeps D, alpha, E in a static device array of
+    NOALLOC_SCRATCH_BYTES per GPU (so they are not returned), and this
+    function allocates nothing either, so every output (gq, gdo with q's
+    shape; gk, gv with k's) must be given.  Calls that overlap on one GPU
+    share that array and must be serialised.  Returns (gq, gk, gv, gdo)."""
+    B, H, N, d, Hkv = _check_inputs((q, dout, uq), (k, v, uk, uv))
+    _check_saved_state(q, o, lse)
+    if any(t is None for t in (gq, gk, gv, gdo)):
+        raise ValueError("fa_bob_noalloc allocates nothing: pass gq, gk, gv and gdo")
+    for t, like, what in ((gq, q, "gq"), (gk, k, "gk"), (gv, k, "gv"), (gdo, q, "gdo")):
+        _f32_like(like, t, what)
+    p = problem(B, H, N, d, _dtype_code(q), scale, int(bool(causal)), Hkv, dropout, seed)
+    _call("fa_bob_noalloc", load_library().fa_bob_noalloc(
+        ctypes.byref(p), tensor_arg(q), tensor_arg(k), tensor_arg(v), tensor_arg(o),
+        ctypes.c_void_p(lse.data_ptr()), tensor_arg(dout), tensor_arg(uq), tensor_arg(uk), tensor_arg(uv),
+        tensor_arg(gq), tensor_arg(gk), tensor_arg(gv), tensor_arg(gdo), _stream(stream)))
+    return gq, gk, gv, gdo
 
 
 def split_workspace(ws, B, H, N):

@@ -1,7 +1,10 @@
 // fa_api.hip -- the C ABI declared in include/fa.h: host-side validation and
-// kernel launches.  No allocation, no synchronisation, no state.
+// kernel launches.  No allocation and no synchronisation; the only state is
+// the per-device address of fa_bob_noalloc's static scratch array.
 #include <math.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "fa.h"
 #include "fa_kernels.hip"
@@ -15,7 +18,8 @@ using fa::Args;
 using fa::bf16;
 using fa::TDesc;
 
-constexpr int kVersion = 1 * 10000 + 2 * 100 + 0;  // 1.1: fa_problem.H_kv; 1.2: dropout, seed
+constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;  // 1.1: fa_problem.H_kv; 1.2: dropout, seed;
+                                                   // 1.3: fa_bob_noalloc
 
 struct Ctx {
   int64_t B, H, N, d;
@@ -374,6 +378,34 @@ struct BobL {
 
 }  // namespace
 
+// Workspace of fa_bob_noalloc: a device array that every call on one GPU
+// shares (each GPU holds its own copy for the life of the process).  Host
+// code never uses its name as an address: the per-device address comes from
+// hipGetSymbolAddress on the first call made with that device current.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Address of the current device's scratch array (looked up once per device).
+fa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return FA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return kVersion; }
@@ -465,7 +497,7 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
 static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o,
                           const float* lse, fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq,
                           fa_tensor gk, fa_tensor gv, fa_tensor gdo, void* workspace, size_t workspace_bytes,
-                          int schedule, int phase, void* stream) {
+                          int schedule, int phase, void* stream, bool use_scratch = false) {
   Ctx c;
   FA_CHECK(check_problem(p, &c));
   if (schedule < 0 || schedule > 2) return FA_ERR_UNSUPPORTED;
@@ -484,6 +516,11 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   FA_CHECK(check_tensor(c, gv, 4));
   FA_CHECK(check_tensor(c, gdo, 4));
   FA_CHECK(check_vec(lse));
+  if (use_scratch) {  // fa_bob_noalloc: the static array, once the arguments passed
+    if (fa_bob_workspace_bytes(p) > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+    FA_CHECK(scratch_of_current_device(&workspace));
+    workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
+  }
   if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 16) return FA_ERR_WORKSPACE;
   if (workspace_bytes < fa_bob_workspace_bytes(p)) return FA_ERR_WORKSPACE;
   Args a = base_args(c);
@@ -518,6 +555,12 @@ fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_
                  fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq, fa_tensor gk, fa_tensor gv,
                  fa_tensor gdo, void* workspace, size_t workspace_bytes, void* stream) {
   return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, workspace, workspace_bytes, 0, -1, stream);
+}
+
+fa_status fa_bob_noalloc(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o,
+                         const float* lse, fa_tensor dout, fa_tensor uq, fa_tensor uk, fa_tensor uv, fa_tensor gq,
+                         fa_tensor gk, fa_tensor gv, fa_tensor gdo, void* stream) {
+  return bob_impl(p, q, k, v, o, lse, dout, uq, uk, uv, gq, gk, gv, gdo, nullptr, 0, 0, -1, stream, true);
 }
 
 fa_status fa_bob_phase(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, const float* lse,

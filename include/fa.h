@@ -190,6 +190,31 @@ fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_bob_noalloc -- fa_bob for callers that cannot allocate device memory
+ * (code being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as fa_bob without the
+ * workspace: D, alpha, E and the row pass's per-row values live in a static
+ * device array of FA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on
+ * each GPU it runs on until the process ends, so D, alpha and E are not
+ * returned.  Nothing in the array needs clearing: the row pass writes every
+ * value the column pass reads.  The array's address on the current device is
+ * looked up on the first call made with that device current; call with the
+ * stream's device current.
+ * Limit: fa_bob_workspace_bytes(p) <= FA_NOALLOC_SCRATCH_BYTES, i.e. about
+ * B*H*N <= 1.19 million rows (N = 262,144 with B*H = 4 fits); a larger
+ * problem returns FA_ERR_WORKSPACE before anything is launched.
+ * Calls that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) share the array and race: serialise them.
+ * Allocates nothing, no torch or library allocator included.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_bob_noalloc(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
+                         fa_tensor o, const float* lse, fa_tensor dout,
+                         fa_tensor uq, fa_tensor uk, fa_tensor uv,
+                         fa_tensor gq, fa_tensor gk, fa_tensor gv, fa_tensor gdo,
+                         void* stream);
+
+/*
  * fa_bob_phase -- one kernel of fa_bob, for per-kernel timing and profiling.
  * Same arguments as fa_bob plus `phase`: 0 launches the row-scalar kernel
  * (writes D; with bf16 inputs the row pass computes D itself and phase 0

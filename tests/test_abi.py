@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 10200  # 1.2.0: fa_problem gained dropout and seed (1.1.0: H_kv)
+    assert lib.fa_version() == 10300  # 1.3.0: fa_bob_noalloc (1.2.0: dropout and seed; 1.1.0: H_kv)
     for code in range(8):
         s = lib.fa_status_str(code).decode()
         assert s and s != "unknown status"
@@ -233,3 +233,31 @@ def test_schedule_checks_tensors_too(lib):
     bad[0] = t(ptr=0)
     assert sched(lib, prob(), 2, -1, bad) == 1
 
+
+def noalloc(lib, p, ts=None):
+    ts = ts or [t() for _ in range(12)]
+    return lib.fa_bob_noalloc(ctypes.byref(p), ts[0], ts[1], ts[2], ts[3], FAKE, ts[4], ts[5], ts[6], ts[7],
+                              ts[8], ts[9], ts[10], ts[11], None)
+
+
+def test_noalloc_validation(lib):
+    """fa_bob_noalloc checks its arguments like fa_bob and refuses a problem
+    whose workspace exceeds its static array, all before touching the GPU."""
+    bad = [t() for _ in range(12)]
+    bad[5] = t(ptr=0)
+    assert noalloc(lib, prob(), bad) == 1
+    assert noalloc(lib, prob(d=96)) == 5
+    small = prob(B=1, H=4, N=65536)
+    big = prob(B=1, H=8, N=262144)
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(small)) <= fa.NOALLOC_SCRATCH_BYTES
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(big)) > fa.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, big) == 6
+    bad = [t() for _ in range(12)]
+    bad[11] = t(ptr=0)
+    assert noalloc(lib, big, bad) == 1  # argument errors come first
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
