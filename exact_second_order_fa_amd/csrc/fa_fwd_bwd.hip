@@ -302,9 +302,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS.  The G query heads of a
 // key/value head are streamed one after another into the same accumulators.
 // DROP ([FlashBoB] appendix G): dP - D = g (dO V^T) - D, so that chain starts
-// at 0 and takes -D after the mask, and dV^T += dO^T (P g).
+// at 0 and takes -D after the mask, and dV^T += dO^T (P g).  At d = 64 two
+// waves share a SIMD (each within 128 VGPRs and 128 AGPRs; the chains of the
+// other wave hide this one's latencies), at d = 128 one.
 template <int D, int TS, bool CAUSAL, bool DROP = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_dkdv_dma_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1))) void
+bwd_dkdv_dma_kernel(Args a) {
   static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
@@ -376,8 +379,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       asm volatile("s_nop 1" : "+v"(s), "+v"(dp));  // VALU write -> MFMA read of C
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        mfma_v(s, rd_row<D, TS>(tq, rd, sub, ks), kf[ks]);
-        mfma_v(dp, rd_row<D, TS>(tdo, rd, sub, ks), vf[ks]);
+        if constexpr (D == 64) {
+          // Two waves per SIMD: short of VGPRs the compiler keeps K and V in
+          // AGPRs and copies them back (a VALU write) right before an MFMA.
+          mfma_v_w(s, rd_row<D, TS>(tq, rd, sub, ks), kf[ks]);
+          mfma_v_w(dp, rd_row<D, TS>(tdo, rd, sub, ks), vf[ks]);
+        } else {
+          mfma_v(s, rd_row<D, TS>(tq, rd, sub, ks), kf[ks]);
+          mfma_v(dp, rd_row<D, TS>(tdo, rd, sub, ks), vf[ks]);
+        }
       }
     };
     f32x16 sb[2], pb[2];
