@@ -8,7 +8,8 @@ the whole-tensor measure) and the last test of a workload prints the
 whole-tensor measure.
 
 * tiny (fp32) and mid: every element, dense / streaming oracle.
-* hd128, long, gpt2c_4k, gpt2c_16k, c128_16k, mqa_32k, mqa128_8k: every
+* hd128, long, gpt2c_4k, gpt2c_16k, c128_16k and the multi-query mqa_2k,
+  mqa_8k, mqa_32k, mqa128_8k: every
   element of every output (O, L, D, alpha, E, dQ, dK, dV, gQ, gK, gV, gdO),
   against the streaming float64 oracle run in-test head by head, split over
   several tests so that each finishes in well under a minute of host time.
@@ -199,7 +200,10 @@ def test_workload_whole_tensors(name, part):
 
 # Multi-query workloads (8 query heads share one key/value head): the rows of
 # the query heads, then the shared head's columns summed over the group.
-MQA = {"mqa_32k": 4, "mqa128_8k": 8}
+# Below 256 key blocks the column kernels split each key block's query heads
+# over several workgroups: mqa_2k into 8 (one head each), mqa_8k and
+# mqa128_8k into 4; mqa_32k does not split.
+MQA = {"mqa_32k": 4, "mqa128_8k": 8, "mqa_8k": 8, "mqa_2k": 8}
 MQA_CASES = [(name, i) for name, per in MQA.items() for i in range(WORKLOADS[name].H // per + 1)]
 
 
