@@ -36,13 +36,13 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
 PEAK_FP32_MFMA_TFLOPS = 157.3
-# The FlashBoB paper's own BoB wall-clock times for these shapes (Table 1: batch 4,
-# 12 heads, causal, bf16 inputs with fp32 reductions), on other GPUs: context
-# printed beside ours, never a target.
+# The FlashBoB paper's own BoB wall-clock times and peak memory for these shapes
+# (Table 1: batch 4, 12 heads, causal, bf16 inputs with fp32 reductions), on
+# other GPUs: context printed beside ours (time, device_bytes), never a target.
 PAGES_MS = {
-    "gpt2c_4k": {"ms": 25.80, "gpu": "A100 80GB", "source": "FlashBoB Table 1, d=64"},
-    "gpt2c_16k": {"ms": 365.73, "gpu": "A100 80GB", "source": "FlashBoB Table 1, d=64"},
-    "c128_16k": {"ms": 263.6, "gpu": "B300", "source": "FlashBoB Table 1, d=128"},
+    "gpt2c_4k": {"ms": 25.80, "peak_mib": 1243, "gpu": "A100 80GB", "source": "FlashBoB Table 1, d=64"},
+    "gpt2c_16k": {"ms": 365.73, "peak_mib": 3372, "gpu": "A100 80GB", "source": "FlashBoB Table 1, d=64"},
+    "c128_16k": {"ms": 263.6, "peak_mib": 4422, "gpu": "B300", "source": "FlashBoB Table 1, d=128"},
 }
 # The pages' schedule ablation (three-pass vs two-pass; GPT-2 Small shape,
 # batch 4, on A100), context only.
@@ -51,6 +51,10 @@ PAGES_ABLATION = {
                  "source": "FlashBoB Table 8"},
     "gpt2c_16k": {"three_pass_ms": 389.14, "two_pass_ms": 365.73, "ratio": 1.06, "gpu": "A100 80GB",
                   "source": "FlashBoB Table 8"},
+    "gpt2c_64k": {"three_pass_ms": 6227.59, "two_pass_ms": 5843.14, "ratio": 1.07, "gpu": "A100 80GB",
+                  "source": "FlashBoB Table 8"},
+    "gpt2c_256k": {"three_pass_ms": 100696.16, "two_pass_ms": 94853.72, "ratio": 1.06, "gpu": "A100 80GB",
+                   "source": "FlashBoB Table 8"},
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bob_pass1_traffic.json")
 KERNEL_SOURCES = ("exact_second_order_fa_amd/csrc/fa_bob.hip", "exact_second_order_fa_amd/csrc/fa_bob_ws.hip",
