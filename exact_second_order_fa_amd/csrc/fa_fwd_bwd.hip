@@ -26,6 +26,14 @@ __device__ inline void mfma_vacc(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 __device__ inline void vfence1(f32x16& a) { asm volatile("s_nop 7\n\ts_nop 4" : "+v"(a)); }
+// d = a * b + c with b resident in AGPRs and c in its own registers (kept):
+// the matrix core reads c after issue, so a write of c's registers must wait
+// 7 wait states, which the instruction carries.
+__device__ inline f32x16 mfma_init_a(bf16x8 a, bf16x8 b, const f32x16& c) {
+  f32x16 d;
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 6" : "=&v"(d) : "v"(a), "a"(b), "v"(c));
+  return d;
+}
 
 // ---------------------------------------------------------------------------
 // Forward: O = softmax(tau Q K^T) V with the online softmax, L = log-sum-exp.
@@ -208,6 +216,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const float Li = row < N ? a.lse[rv + row] : 0.0f;
   const float Di = row < N ? a.D[rv + row] : 0.0f;
   const float nl2 = -Li * kLog2e;
+  // At d = 64 without dropout the dP chains start from -D (the MFMA's C
+  // operand), so dP - D comes out of the matrix core (fa_bwd 2-3 % faster;
+  // at d = 128 it measured no faster and is not used).
+  constexpr bool NEGD = D == 64 && !DROP;
+  f32x16 negd;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) negd[e] = -Di;
   Reader<D, TS> rd;
   rd.init();
 
@@ -242,7 +257,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           mfma_va(s, xk, qf[ks]);
         }
         if (ks == 0) {
-          dp = mfma_first_a(xv, df[0]);
+          dp = NEGD ? mfma_init_a(xv, df[0], negd) : mfma_first_a(xv, df[0]);
         } else {
           mfma_va(dp, xv, df[ks]);
         }
@@ -264,7 +279,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int idx = 0; idx < 16; ++idx) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], a.c1, nl2));
-        cds.f[idx >> 3][idx & 7] = (bf16)(p * (DROP ? fmaf(dm.at(a, sub & 1, idx), dp[idx], -Di) : dp[idx] - Di));
+        cds.f[idx >> 3][idx & 7] =
+            (bf16)(p * (DROP ? fmaf(dm.at(a, sub & 1, idx), dp[idx], -Di) : NEGD ? dp[idx] : dp[idx] - Di));
       }
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
