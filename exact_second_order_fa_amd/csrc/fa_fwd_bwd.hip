@@ -37,16 +37,23 @@ __device__ inline f32x16 mfma_init_a(bf16x8 a, bf16x8 b, const f32x16& c) {
 
 // ---------------------------------------------------------------------------
 // Forward: O = softmax(tau Q K^T) V with the online softmax, L = log-sum-exp.
-// Per 32-key sub-tile: S^T = K Q^T (keys on M); the running maximum m (log2
-// domain) and sum l; O <- O * exp2(m_old - m_new) + V^T P.  The rescale is
-// skipped when no row's maximum moved, which after the first tiles is the
-// common case.  The scores of sub-tile s + 1 are issued before the
-// elementwise work of s, so the matrix cores and the VALU overlap.
+// Per 32-key sub-tile: S^T = K Q^T (keys on M); a reference maximum m (log2
+// domain) and the sum l; O <- O * exp2(m_old - m_new) + V^T P.  The softmax
+// is the same for any reference, so m moves only when a row's exponentials
+// against it would exceed 2^16 (or it is still -inf): in the common case a
+// sub-tile costs one FMA, one exp2, one add and half a conversion per score,
+// with no maximum, no rescale and no second exp2.  The scores of sub-tile
+// s + 1 are issued before the elementwise work of s, so the matrix cores and
+// the VALU overlap.
 //
 // DROP: dropout with the scaled keep mask g ([FlashBoB] appendix G): O takes
 // (P g) V while the row sum and L keep P.  The mask of each pair of sub-tiles
 // comes from one shared generator call per lane (DropRow), issued behind the
 // score MFMAs of the next sub-tile.
+// Largest partial row sum (16 exponentials of one lane) accepted against a
+// stale reference maximum; it bounds every exponential by 2^16.
+constexpr float kLazyBound = 65536.0f;
+
 template <int D, int TS, bool CAUSAL, bool DROP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_dma_kernel(Args a) {
   static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
@@ -118,31 +125,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (DROP) {
         if (sub % 2 == 0) dm.init(a, wk.bh, row, t * TS + sub * 32);
       }
-      float mx = s[0];
-#pragma unroll
-      for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, s[idx]);
-      mx = half_max(mx);
-      const float mn = fmaxf(m, mx * c1);
-      const float ms = (mn == -INFINITY) ? 0.0f : mn;
-      const float sc = __builtin_amdgcn_exp2f(m - ms);
       Chain<bf16> cp;
-      float ps = 0.0f;
+      float ps;
+      auto expo = [&](float ref) {
+        ps = 0.0f;
 #pragma unroll
-      for (int idx = 0; idx < 16; ++idx) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], c1, -ms));
-        ps += p;
-        cp.f[idx >> 3][idx & 7] = (bf16)(DROP ? p * dm.at(a, sub & 1, idx) : p);
-      }
-      lsum = fmaf(lsum, sc, ps);
-      m = mn;
-      if (__any(sc != 1.0f)) {
+        for (int idx = 0; idx < 16; ++idx) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[idx], c1, -ref));
+          ps += p;
+          cp.f[idx >> 3][idx & 7] = (bf16)(DROP ? p * dm.at(a, sub & 1, idx) : p);
+        }
+      };
+      // Lazy maximum: the exponentials are taken against the reference m
+      // of the earlier tiles.  Only when some row's partial sum leaves
+      // (0, kLazyBound] -- a score far above m, or m still -inf -- does the
+      // wave take the maximum of the sub-tile, move m and rescale.
+      expo(m);
+      if (__any(!(ps <= kLazyBound))) {
+        float mx = s[0];
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          vfence1(acc[db]);
+        for (int idx = 1; idx < 16; ++idx) mx = fmaxf(mx, s[idx]);
+        mx = half_max(mx);
+        const float mn = fmaxf(m, mx * c1);
+        const float ms = (mn == -INFINITY) ? 0.0f : mn;
+        const float sc = __builtin_amdgcn_exp2f(m - ms);
+        expo(ms);
+        lsum *= sc;
+        m = mn;
+        if (__any(sc != 1.0f)) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[db][e] *= sc;
+          for (int db = 0; db < NDB; ++db) {
+            vfence1(acc[db]);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[db][e] *= sc;
+          }
         }
       }
+      lsum += ps;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
