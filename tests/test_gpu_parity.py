@@ -12,7 +12,7 @@ dense oracle.  The full-size workloads are in test_gpu_workloads.py.
 import numpy as np
 import pytest
 
-from fa_inputs import make_inputs
+from fa_inputs import bf16_bits_to_f32, f32_to_bf16_bits, make_inputs
 from oracle import bob_dense, bob_dense_gqa
 from tests.gpu_helpers import NAMES, host, rel, run_path, say, to_device
 
@@ -33,10 +33,13 @@ def oracle_heads(f64, scale, causal=False):
     return out
 
 
-def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd", causal=False, schedule=None):
+def check_case(B, H, N, d, dtype, seed, scale=None, qk=1.0, cot=1.0, layout="bhnd", causal=False, schedule=None,
+               shape_inputs=None):
     say(f"case B={B} H={H} N={N} d={d} {dtype} seed={seed} scale={scale} layout={layout} causal={causal} "
         f"schedule={schedule}")
     raw, f64 = make_inputs(B, H, N, d, seed, dtype, cot_std=cot, qk_gain=qk)
+    if shape_inputs is not None:
+        shape_inputs(raw, f64)
     tau = scale if scale is not None else 1.0 / np.sqrt(d)
     got = run_path(to_device(raw, dtype, layout), scale=scale, layout=layout, causal=causal, schedule=schedule)
     ref = oracle_heads(f64, tau, causal)
@@ -103,6 +106,31 @@ def test_peaked_rows():
     """Q, K scaled by 2 (peaked softmax rows) and small cotangents."""
     check_case(1, 2, 512, 64, "bf16", 303, qk=2.0, cot=0.1)
     check_case(1, 1, 256, 128, "bf16", 304, qk=2.0, cot=0.1)
+
+
+def _rising_keys(raw, f64):
+    """Key norms growing tenfold along the sequence, so that the row maxima
+    keep rising (the reference maximum of the forward moves about twice per
+    row besides the first tile), and key 900 of every head set along q_950
+    with norm 64: row 950's score on it is about 40 above every other one
+    (natural log), far beyond the 2^16 factor the forward accepts against an
+    earlier maximum, so its reference maximum has to jump.  Values are
+    rounded to bf16 for both sides."""
+    k = f64["k"].copy()
+    n = k.shape[2]
+    k *= (1.0 + 9.0 * np.arange(n) / n)[None, None, :, None]
+    q950 = f64["q"][:, :, 950]
+    k[:, :, 900] = 64.0 * q950 / np.linalg.norm(q950, axis=-1, keepdims=True)
+    bits = f32_to_bf16_bits(k.astype(np.float32))
+    raw["k"] = bits
+    f64["k"] = bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_reference_maximum(causal):
+    """Rising scores and one late outlier (see _rising_keys), N = 1000 (eight
+    key tiles with a ragged one), d = 64: every output against the oracle."""
+    check_case(1, 2, 1000, 64, "bf16", 309, causal=causal, shape_inputs=_rising_keys)
 
 
 def test_strided_layout():
