@@ -165,6 +165,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(NSLICE == 4 || NSLICE == 8, "slices");
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
   __shared__ __attribute__((aligned(16))) float kbias[TS];  // chain init of a ragged last tile
+  // At d = 128 with dropout the mask words and the fifth operand chain leave
+  // too few VGPRs for the resident U_Q rows (the AGPRs hold the four output
+  // accumulators): each lane parks its U_Q fragments in LDS and reads them
+  // back where the F chain takes them, instead of the compiler spilling to
+  // scratch inside the tile loop.  That fills the 160 KB of LDS exactly, so
+  // this instance masks a ragged last tile element by element instead of
+  // keeping the bias row.
+  constexpr int NPARK = DROP && D == 128 ? NKS : 0;
+  __shared__ __attribute__((aligned(16))) bf16x8 uq_park[NPARK ? NPARK * kThreads : 1];
 
   const Work wk = work_item(a, CAUSAL);
   const int N = a.N;
@@ -185,12 +194,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   Dma<D, TS, 4> dma;
   dma.init(src);
   dma.copy(0, N, lds);
-  fill_bias<TS>(kbias, (nt - 1) * TS, N);
+  if constexpr (NPARK == 0) fill_bias<TS>(kbias, (nt - 1) * TS, N);
 
   bf16x8 qf[NKS], uqf[NKS], df[NKS];
   load_resident<bf16, D>(qf, q.p, q.sn, row, N, a.pow2);
   load_resident<bf16, D>(uqf, uq.p, uq.sn, row, N, a.pow2);
   load_resident<bf16, D>(df, dout.p, dout.sn, row, N, 1.0f);
+#pragma unroll
+  for (int ks = 0; ks < NPARK; ++ks) uq_park[ks * kThreads + threadIdx.x] = uqf[ks];
+  // U_Q fragment ks: from the registers, or read back from this lane's own
+  // LDS slot (volatile, so that the reads stay where they are used).
+  auto uq_frag = [&](int ks) {
+    if (ks < NPARK) return *reinterpret_cast<volatile bf16x8*>(&uq_park[ks * kThreads + threadIdx.x]);
+    return uqf[ks];
+  };
   const int64_t rv = (int64_t)wk.bh * N;
   const float Li = row < N ? a.lse[rv + row] : 0.0f;
   // Two-pass: D is computed here (no separate row-scalar kernel) and written
@@ -238,8 +255,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
     auto scores = [&](int sub, f32x16& s, f32x16& f, f32x16& dp, f32x16& c) {
-      if constexpr (MODE == 1) {
+      if constexpr (MODE == 1 && NPARK == 0) {
         s = row_init<TS>(kbias, sub);
+      } else if constexpr (MODE == 1) {
+#pragma unroll
+        for (int idx = 0; idx < 16; ++idx) s[idx] = (t * TS + sub * 32 + acc_pos(idx, hh) < N) ? 0.0f : -INFINITY;
+        asm volatile("s_nop 1" : "+v"(s));  // VALU write -> MFMA read of C
       } else if constexpr (MODE == 2) {
 #pragma unroll
         for (int idx = 0; idx < 16; ++idx)
@@ -258,11 +279,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           macc(s, xk, qf[ks]);
         }
         if (ks == 0) {
-          f = first(xk, uqf[0]);
+          f = first(xk, uq_frag(0));
           dp = first(xv, df[0]);
           c = first(xuv, df[0]);
         } else {
-          macc(f, xk, uqf[ks]);
+          macc(f, xk, uq_frag(ks));
           macc(dp, xv, df[ks]);
           macc(c, xuv, df[ks]);
         }
