@@ -120,6 +120,7 @@ Args base_args(const Ctx& c) {
   a.G = (int)c.G;
   a.gs = (int)c.G;
   a.nsplit = 1;
+  a.rs = 1;
   a.part = nullptr;
   a.N = (int)c.N;
   a.tau = c.tau;
@@ -159,6 +160,25 @@ int group_split(const Ctx& c) {
   for (int s = 2; s < c.G; ++s)
     if (c.G % s == 0 && cols * s >= 256) return s;
   return (int)c.G;
+}
+
+// Row split of the BoB column pass, on top of the group split g: still fewer
+// than 256 workgroups (few key blocks and few query heads per key/value head,
+// e.g. multi-query attention at N = 2048: 16 x 8) and not causal, each
+// query head's rows are cut into r ranges of at least two 128-row blocks
+// (r the smallest power of two that reaches 256), whose key-side sums are
+// further partials of the block's.
+int row_split(const Ctx& c, int g) {
+  if (!c.bf || c.causal) return 1;
+  const int64_t nblk = (c.N + fa::kResRows - 1) / fa::kResRows;
+  const int64_t cols = c.B * c.Hkv * nblk * g;
+  int r = 1;
+  while (cols * r < 256 && nblk / (2 * r) >= 2) r *= 2;
+  return r;
+}
+int bob_nsplit(const Ctx& c) {
+  const int g = group_split(c);
+  return g * row_split(c, g);
 }
 
 // Floats of the partial key-side sums of a group split: [2][nsplit][B * H_kv][N][d].
@@ -433,7 +453,7 @@ size_t fa_bwd_workspace_bytes(const fa_problem* p) {
 size_t fa_bob_workspace_bytes(const fa_problem* p) {
   Ctx c;
   if (check_problem(p, &c) != FA_OK) return 0;
-  return (bob_part_offset(c) + split_floats(c, group_split(c))) * sizeof(float);
+  return (bob_part_offset(c) + split_floats(c, bob_nsplit(c))) * sizeof(float);
 }
 
 fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
@@ -542,8 +562,10 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   a.alpha = a.D + nrow;
   a.E = a.D + 2 * nrow;
   a.ps = a.D + 3 * nrow;
-  a.nsplit = group_split(c);
-  a.gs = (int)(c.G / a.nsplit);
+  const int gsplit = group_split(c);
+  a.gs = (int)(c.G / gsplit);
+  a.rs = row_split(c, gsplit);
+  a.nsplit = gsplit * a.rs;
   a.part = a.nsplit > 1 ? a.D + bob_part_offset(c) : nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();

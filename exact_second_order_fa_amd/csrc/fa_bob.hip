@@ -648,7 +648,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   // Causal: query tiles before this key block's first key are skipped; tiles
   // below t_diag cross the diagonal and are masked element by element.
-  const int t_begin = CAUSAL ? wk.rb * kResRows / TS : 0;
+  // A row split (non-causal only) gives this workgroup tiles [t_begin, t_end)
+  // of every query head; its key-side sums are one partial of the block's.
+  const int t_begin = CAUSAL ? wk.rb * kResRows / TS : (int)((int64_t)nt * wk.rr / a.rs);
+  const int t_end = CAUSAL ? nt : (int)((int64_t)nt * (wk.rr + 1) / a.rs);
   const int t_diag = CAUSAL ? (wk.rb * kResRows + kResRows + TS - 1) / TS : 0;
   copy_tile(0, t_begin, lds);
 
@@ -1012,7 +1015,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         dma_wait();
         __syncthreads();
         // The next tile: t + 1 of this head, else the next head's first.
-        const bool wrap = t + 1 >= nt;
+        const bool wrap = t + 1 >= t_end;
         const int gn = wrap ? g + 1 : g, tn = wrap ? t_begin : t + 1;
         if (gn < a.gs) copy_tile(gn, tn, lds + ((u + 1) & 1) * STAGE);
         tile_body(t, u & 1, g, mode_c);
@@ -1021,7 +1024,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       acc_fence2<NDB>(ak, av);
     };
     if constexpr (CAUSAL) run(t_begin, min(t_diag, nt), std::integral_constant<int, 2>{});
-    run(CAUSAL ? min(t_diag, nt) : 0, nt, std::integral_constant<int, 0>{});
+    run(CAUSAL ? min(t_diag, nt) : t_begin, t_end, std::integral_constant<int, 0>{});
   }
 
   acc_fence2<NDB>(ak, av);

@@ -38,7 +38,8 @@ struct Args {
   float* part;                         // key-side partial sums of a split group (or null), see GroupSplit
   int B, H, N;
   int Hk, G;                 // key/value heads and query heads per key/value head (H = Hk * G)
-  int gs, nsplit;            // column kernels: query heads per workgroup (G / nsplit) and splits of a group
+  int gs, nsplit;            // column kernels: query heads per workgroup and partial sums per key block
+  int rs;                    // column kernels: query-row ranges per head subset (nsplit = G / gs * rs)
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
   uint64_t seed;             // dropout: generator key
   uint32_t drop_thr;         // dropout: keep an element iff its byte >= drop_thr (1..255)
@@ -66,7 +67,8 @@ __device__ inline float* head_out(const TDesc& t, int b, int h) {
 //     over the group inside one workgroup).
 struct Work {
   int bh, b, h, hk, rb;
-  int sp;  // column kernels: which split of the group's query heads (0 without a split)
+  int sp;  // column kernels: which partial sum of the key block (0 without a split)
+  int rr;  // column kernels: which range of the query rows (0 without a row split)
 };
 
 // heavy_first: causal row-side kernels do work proportional to rb + 1; the
@@ -100,7 +102,9 @@ __device__ inline Work work_item_cols(const Args& a) {
   r.rb = w2 % nblk;
   r.b = r.bh / a.Hk;
   r.hk = r.bh % a.Hk;
-  r.h = r.hk * a.G + r.sp * a.gs;
+  const int sh = r.sp / a.rs;  // subset of the group's query heads
+  r.rr = r.sp - sh * a.rs;
+  r.h = r.hk * a.G + sh * a.gs;
   return r;
 }
 

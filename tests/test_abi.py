@@ -99,6 +99,23 @@ def test_workspace_sizes(lib):
     mid = prob(1, 8, 8192, 64, Hkv=1)
     assert lib.fa_bob_workspace_bytes(ctypes.byref(mid)) == \
         (_align64(3 * 8 * 8192 + 4 * 8 * 8192) + 2 * 4 * 8192 * 64) * 4
+    # Still short of 256 after splitting the group (1 x 1 x 16 key blocks x
+    # G = 8 at N = 2048), the non-causal column pass also cuts each query
+    # head's rows into two ranges: 16 partials.  Causal: the group split only.
+    mqa2k = prob(1, 8, 2048, 64, Hkv=1)
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(mqa2k)) == \
+        (_align64(3 * 8 * 2048 + 4 * 8 * 2048) + 2 * 16 * 2048 * 64) * 4
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 8, 2048, 64, Hkv=1, causal=1))) == \
+        (_align64(3 * 8 * 2048 + 4 * 8 * 2048) + 2 * 8 * 2048 * 64) * 4
+    # Multi-head with few blocks (4 heads x 32 blocks = 128): two row ranges.
+    # Ranges keep at least two 128-row blocks, so N = 300 (3 blocks) is never cut.
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 4, 4096, 64))) == \
+        (_align64(3 * 4 * 4096 + 4 * 4 * 4096) + 2 * 2 * 4 * 4096 * 64) * 4
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 1, 300, 64))) == \
+        _align64(3 * 300 + 4 * 384) * 4
+    # The first backward keeps the group split only.
+    assert lib.fa_bwd_workspace_bytes(ctypes.byref(mqa2k)) == \
+        (_align64(8 * 2048 + 2 * 8 * 2048) + 2 * 8 * 2048 * 64) * 4
     # fp32 inputs run the portable kernels, which never split.
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, Hkv=1, dt=fa.FA_FP32))) == \
         lib.fa_bob_workspace_bytes(ctypes.byref(prob(2, 3, 130, 64, dt=fa.FA_FP32)))

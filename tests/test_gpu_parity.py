@@ -215,6 +215,7 @@ def check_case_gqa(B, H, Hkv, N, d, dtype, seed, causal=False, layout="bhnd", sc
     (1, 8, 2, 300, 128, False),  # d = 128
     (1, 4, 2, 257, 128, True),
     (1, 3, 3, 70, 64, False),    # H_kv = H (multi-head through the grouped path)
+    (1, 8, 1, 600, 128, False),  # MQA, d = 128, column pass split over heads and two row ranges
 ])
 def test_gqa_bf16_shapes(B, H, Hkv, N, d, causal):
     check_case_gqa(B, H, Hkv, N, d, "bf16", 800 + H + Hkv + N + d, causal=causal)

@@ -201,9 +201,10 @@ def test_workload_whole_tensors(name, part):
 # Multi-query workloads (8 query heads share one key/value head): the rows of
 # the query heads, then the shared head's columns summed over the group.
 # Below 256 key blocks the column kernels split each key block's query heads
-# over several workgroups: mqa_2k into 8 (one head each), mqa_8k and
-# mqa128_8k into 4; mqa_32k does not split.
-MQA = {"mqa_32k": 4, "mqa128_8k": 8, "mqa_8k": 8, "mqa_2k": 8}
+# over several workgroups: mqa_8k and mqa128_8k into 4; mqa_32k does not
+# split; mqa_2k and mqa128_2k into 8 (one head each) and, in the BoB column
+# pass, each head's rows into two ranges (16 partial sums per key block).
+MQA = {"mqa_32k": 4, "mqa128_8k": 8, "mqa_8k": 8, "mqa_2k": 8, "mqa128_2k": 8}
 MQA_CASES = [(name, i) for name, per in MQA.items() for i in range(WORKLOADS[name].H // per + 1)]
 
 
