@@ -20,8 +20,9 @@ LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_OK = 0
 # fa_version() the binding needs: 1.1 added fa_problem.H_kv (an older library
-# would read key-side tensors with the query-head count), 1.3 fa_bob_noalloc.
-MIN_VERSION = 10300
+# would read key-side tensors with the query-head count), 1.3 fa_bob_noalloc,
+# 1.4 a 64 MiB no-alloc array (NOALLOC_SCRATCH_BYTES below must match).
+MIN_VERSION = 10400
 STATUS_NAMES = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_STRIDE", 4: "FA_ERR_DTYPE",
     5: "FA_ERR_UNSUPPORTED", 6: "FA_ERR_WORKSPACE", 7: "FA_ERR_HIP",
@@ -32,7 +33,7 @@ FA_BF16, FA_FP32 = 0, 1
 SYMBOLS = ("fa_version", "fa_status_str", "fa_fwd", "fa_bwd_workspace_bytes", "fa_bwd",
            "fa_bob_workspace_bytes", "fa_bob", "fa_bob_noalloc", "fa_bob_phase", "fa_bob_schedule")
 # Size of fa_bob_noalloc's static device workspace (FA_NOALLOC_SCRATCH_BYTES).
-NOALLOC_SCRATCH_BYTES = 32 << 20
+NOALLOC_SCRATCH_BYTES = 64 << 20
 # Schedules of fa_bob_schedule (include/fa.h).
 SCHED_TWO_PASS, SCHED_TWO_PASS_1WAVE, SCHED_THREE_PASS = 0, 1, 2
 

@@ -18,8 +18,9 @@ using fa::Args;
 using fa::bf16;
 using fa::TDesc;
 
-constexpr int kVersion = 1 * 10000 + 3 * 100 + 0;  // 1.1: fa_problem.H_kv; 1.2: dropout, seed;
-                                                   // 1.3: fa_bob_noalloc
+constexpr int kVersion = 1 * 10000 + 4 * 100 + 0;  // 1.1: fa_problem.H_kv; 1.2: dropout, seed;
+                                                   // 1.3: fa_bob_noalloc; 1.4: split partial sums in
+                                                   // fa_bob's workspace, 64 MiB no-alloc array
 
 struct Ctx {
   int64_t B, H, N, d;
@@ -121,7 +122,9 @@ Args base_args(const Ctx& c) {
   a.gs = (int)c.G;
   a.nsplit = 1;
   a.rs = 1;
+  a.ks = 1;
   a.part = nullptr;
+  a.kpart = nullptr;
   a.N = (int)c.N;
   a.tau = c.tau;
   a.pow2 = c.pow2;
@@ -181,6 +184,25 @@ int bob_nsplit(const Ctx& c) {
   return g * row_split(c, g);
 }
 
+// Key split of the bf16 two-pass row pass (no dropout, not causal): with
+// fewer than 256 row workgroups (B * H * ceil(N / 128); multi-query at
+// N = 2048: 128) each row block's keys are cut into k ranges of at least two
+// 128-key blocks (k the smallest power of two reaching 256), whose raw sums a
+// sum kernel adds and finishes (bob_ksplit_sum_kernel).
+int key_split(const Ctx& c) {
+  if (!c.bf || c.causal || c.drop) return 1;
+  const int64_t nblk = (c.N + fa::kResRows - 1) / fa::kResRows;
+  const int64_t rows = c.B * c.H * nblk;
+  int k = 1;
+  while (rows * k < 256 && nblk / (2 * k) >= 2) k *= 2;
+  return k;
+}
+// Floats of the key-split partial sums: [k][3][B*H][N] row sums and
+// [k][4][B*H][N][d] accumulators.
+size_t ksplit_floats(const Ctx& c, int k) {
+  return k > 1 ? (size_t)k * (size_t)(c.B * c.H * c.N) * (3 + 4 * (size_t)c.d) : 0;
+}
+
 // Floats of the partial key-side sums of a group split: [2][nsplit][B * H_kv][N][d].
 size_t split_floats(const Ctx& c, int nsplit) {
   return nsplit > 1 ? 2 * (size_t)nsplit * (size_t)(c.B * c.Hkv * c.N) * (size_t)c.d : 0;
@@ -193,6 +215,7 @@ size_t align64(size_t f) { return (f + 63) / 64 * 64; }
 size_t bob_part_offset(const Ctx& c) {
   return align64(3 * (size_t)(c.B * c.H * c.N) + 4 * (size_t)(c.B * c.H) * (size_t)padded_rows(c));
 }
+size_t bob_kpart_offset(const Ctx& c) { return align64(bob_part_offset(c) + split_floats(c, bob_nsplit(c))); }
 size_t bwd_part_offset(const Ctx& c) {
   return align64((size_t)(c.B * c.H * c.N) + 2 * (size_t)(c.B * c.H) * (size_t)padded_rows(c));
 }
@@ -341,13 +364,26 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
           hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C, 1>), g, b, 0, st, a);
       }
     } else if (want(1)) {
+      // Two-pass row pass, a.ks workgroups per row block (key split).
+      const dim3 gk(grid_rows(c) * a.ks);
       if constexpr (D == 64) {
-        if (schedule == 0)
+        if (schedule == 0 && a.ks > 1) {  // never causal (key_split)
+          if constexpr (!C)
+            hipLaunchKernelGGL((fa::bob_pass1_ws_kernel<RHO1, C, true>), gk, dim3(2 * fa::kThreads), 0, st, a);
+        } else if (schedule == 0)
           hipLaunchKernelGGL((fa::bob_pass1_ws_kernel<RHO1, C>), g, dim3(2 * fa::kThreads), 0, st, a);
         else
-          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C>), g, b, 0, st, a);
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C>), gk, b, 0, st, a);
+      } else if (a.ks > 1) {  // never causal (key_split)
+        if constexpr (!C)
+          hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C, 0, false, true>), gk, b, 0, st, a);
       } else {
         hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C>), g, b, 0, st, a);
+      }
+      if (a.ks > 1) {
+        const int64_t threads = (int64_t)(c.B * c.H) * padded_rows(c) * (D / 4);
+        hipLaunchKernelGGL((fa::bob_ksplit_sum_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                           st, a);
       }
     }
     if (want(col_phase)) {
@@ -453,7 +489,7 @@ size_t fa_bwd_workspace_bytes(const fa_problem* p) {
 size_t fa_bob_workspace_bytes(const fa_problem* p) {
   Ctx c;
   if (check_problem(p, &c) != FA_OK) return 0;
-  return (bob_part_offset(c) + split_floats(c, bob_nsplit(c))) * sizeof(float);
+  return (bob_kpart_offset(c) + ksplit_floats(c, key_split(c))) * sizeof(float);
 }
 
 fa_status fa_fwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v, fa_tensor o, float* lse,
@@ -567,6 +603,10 @@ static fa_status bob_impl(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tens
   a.rs = row_split(c, gsplit);
   a.nsplit = gsplit * a.rs;
   a.part = a.nsplit > 1 ? a.D + bob_part_offset(c) : nullptr;
+  // Only the two-pass schedule's row passes split their keys (not the
+  // single-wave baseline of the ablation nor the three-pass schedule).
+  a.ks = schedule == 0 ? key_split(c) : 1;
+  a.kpart = a.ks > 1 ? a.D + bob_kpart_offset(c) : nullptr;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   dispatch3<BobL>(c, a, st, schedule, phase);

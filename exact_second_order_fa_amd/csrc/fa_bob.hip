@@ -154,9 +154,13 @@ __device__ inline void acc_fence2(f32x16 (&a)[NDB], f32x16 (&b)[NDB]) {
 // P g and P F g; alpha, E°, Om, R' and Bk keep P.  The mask of each pair of
 // sub-tiles comes from one shared generator call per lane (DropRow), issued
 // while the score MFMAs of the first of them are in flight.
-template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL, int SCHED = 0, bool DROP = false>
+// KSPLIT: the key-split instance (a.ks > 1, see key_range): a range of the
+// keys and raw partial sums instead of the epilogue.  Its own instance, so
+// that the unsplit kernels keep their register allocation.
+template <int D, int TS, bool RHO1, bool SPLIT, bool CAUSAL, int SCHED = 0, bool DROP = false, bool KSPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass1_dma_kernel(Args a) {
   static_assert(!(DROP && SCHED != 0), "the three-pass schedule has no dropout variant");
+  static_assert(!KSPLIT || (!CAUSAL && SCHED == 0 && !DROP), "the key split serves the two-pass schedule only");
   static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
@@ -184,16 +188,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, wk.b, wk.hk), head_of<bf16>(a.v, wk.b, wk.hk),
                           head_of<bf16>(a.uk, wk.b, wk.hk), head_of<bf16>(a.uv, wk.b, wk.hk)};
   const int nt = (N + TS - 1) / TS;
-  // Causal: key tiles past this row block's last row are skipped, and the
-  // tiles from t_diag on cross the diagonal and are masked element by element.
-  const int t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
+  // Key tiles [t_begin, t_end).  Causal: key tiles past this row block's last
+  // row are skipped, and the tiles from t_diag on cross the diagonal and are
+  // masked element by element.  Key split (two-pass, no dropout): this
+  // workgroup's range of the keys.
+  int t_begin = 0, t_end = CAUSAL ? min(nt, (wk.rb * kResRows + kResRows + TS - 1) / TS) : nt;
+  if constexpr (KSPLIT) key_range(a, wk.kk, nt, t_begin, t_end);
   const int t_diag = CAUSAL ? wk.rb * kResRows / TS : nt;
-  const bool ragged = !CAUSAL && (N % TS) != 0;
+  const bool ragged = !CAUSAL && (N % TS) != 0 && t_end == nt;
 
   // Start the first tile's copy before anything else.
   Dma<D, TS, 4> dma;
   dma.init(src);
-  dma.copy(0, N, lds);
+  dma.copy(t_begin * TS, N, lds + (t_begin & 1) * STAGE);
   if constexpr (NPARK == 0) fill_bias<TS>(kbias, (nt - 1) * TS, N);
 
   bf16x8 qf[NKS], uqf[NKS], df[NKS];
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     run(0, t_diag, std::integral_constant<int, 0>{});
     run(t_diag, t_end, std::integral_constant<int, 2>{});
   } else {
-    run(0, ragged ? nt - 1 : nt, std::integral_constant<int, 0>{});
+    run(t_begin, ragged ? nt - 1 : t_end, std::integral_constant<int, 0>{});
     if (ragged) run(nt - 1, nt, std::integral_constant<int, 1>{});
   }
 
@@ -433,6 +440,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float esum = half_sum(eo_p);
   const float eo = SCHED == 0 ? esum : esum + Ai * Di;  // E° = E + alpha D
   const float eob = half_sum(eob_p);
+  if constexpr (KSPLIT) {
+    // Key split: this key range's raw sums; bob_ksplit_sum_kernel does the rest.
+    if (row < N && hh == 0) {
+      kpart_rowsum(a, wk.kk, 0, wk.bh)[row] = alpha;
+      kpart_rowsum(a, wk.kk, 1, wk.bh)[row] = eo;
+      kpart_rowsum(a, wk.kk, 2, wk.bh)[row] = eob;
+      if (wk.kk == 0) a.D[rv + row] = Di;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      store_out(kpart_acc<D>(a, wk.kk, 0, wk.bh), D, row, N, db, [&](int idx) { return ag[db][idx]; });
+      store_out(kpart_acc<D>(a, wk.kk, 1, wk.bh), D, row, N, db, [&](int idx) { return aom[db][idx]; });
+      store_out(kpart_acc<D>(a, wk.kk, 2, wk.bh), D, row, N, db, [&](int idx) { return ar[db][idx]; });
+      store_out(kpart_acc<D>(a, wk.kk, 3, wk.bh), D, row, N, db, [&](int idx) { return abk[db][idx]; });
+    }
+    return;
+  }
   if (row < N && hh == 0) {
     if constexpr (SCHED == 0) {
       a.alpha[rv + row] = alpha;

@@ -33,22 +33,36 @@
 namespace fa {
 
 // d += a * b with every operand in VGPRs (no AGPRs in this kernel: the two
-// waves of a SIMD share 512 registers).
+// waves of a SIMD share 512 registers).  W: with the two wait states of a
+// VALU write in front, for the key-split instance, whose register allocation
+// gathers some operands with v_mov right before the MFMA.
+template <bool W = false>
 __device__ inline void mfma_vv(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  if constexpr (W)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
+template <bool W = false>
 __device__ inline f32x16 mfma_vv_first(bf16x8 a, bf16x8 b) {
   f32x16 d;
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  if constexpr (W)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
   return d;
 }
 // d = a * b + c, with c in its own registers (kept).  The matrix core reads
 // c after issue, so a write of c's registers must wait 7 wait states; the
 // compiler does not know that about an asm MFMA (it may reuse them right
 // after the last one), so the wait is part of the instruction here.
+template <bool W = false>
 __device__ inline f32x16 mfma_vv_init(bf16x8 a, bf16x8 b, const f32x16& c) {
   f32x16 d;
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 6" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  if constexpr (W)
+    asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 6" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+  else
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 6" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
   return d;
 }
 __device__ inline void vfence4(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
@@ -89,7 +103,8 @@ struct WsDma {
   uint32_t offt[2];     // per-lane offset inside a block
   int jl, b, t0;
 
-  __device__ inline void init(const HeadPtr<bf16>* src) {
+  // row_start: the first row the copies start from (a multiple of 32).
+  __device__ inline void init(const HeadPtr<bf16>* src, int row_start) {
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     b = wave & 3;      // block (8 rows) inside each tensor tile
@@ -102,7 +117,7 @@ struct WsDma {
       base[k] = reinterpret_cast<const char*>(h.p);
       rs[k] = h.sn * 2;
       offt[k] = (uint32_t)(jl * (int)rs[k] + 16 * q);
-      next[k] = base[k] + b * 8 * rs[k];
+      next[k] = base[k] + (int64_t)(row_start + b * 8) * rs[k];
     }
   }
 
@@ -125,8 +140,12 @@ struct WsDma {
   }
 };
 
-template <bool RHO1, bool CAUSAL>
+// KSPLIT: the key-split instance (a.ks > 1, see key_range): a range of the
+// keys and raw partial sums instead of the epilogue, in its own instance so
+// that the unsplit kernel is compiled without it.
+template <bool RHO1, bool CAUSAL, bool KSPLIT = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void bob_pass1_ws_kernel(Args a) {
+  static_assert(!(KSPLIT && CAUSAL), "the key split is not causal");
   constexpr int D = 64, TS = 32, NKS = 4, NDB = 2;
   typedef SwTile<D, TS> W;
   constexpr int NSTAGE = 5;
@@ -144,7 +163,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float rowx[4][32];  // alpha handed from producer to consumer
 
   const int nblk = (a.N + kResRows - 1) / kResRows;
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int wid0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int kk = KSPLIT ? wid0 / (a.B * a.H * nblk) : 0;  // key range
+  const int wid = wid0 - kk * (a.B * a.H * nblk);
   // Causal: the largest row blocks of a head first (see work_item).
   const int bh = wid / nblk, rb = CAUSAL ? nblk - 1 - wid % nblk : wid % nblk, bb = bh / a.H, hd = bh % a.H,
             hk = hd / a.G;
@@ -158,11 +179,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   HeadPtr<bf16> src[4] = {head_of<bf16>(a.k, bb, hk), head_of<bf16>(a.v, bb, hk), head_of<bf16>(a.uk, bb, hk),
                           head_of<bf16>(a.uv, bb, hk)};
-  const int nt = CAUSAL ? min((N + TS - 1) / TS, (r0 + kResRows) / TS) : (N + TS - 1) / TS;
+  // Key tiles kt0 .. kt0 + nt - 1; slot and tile numbers below count from kt0.
+  int kt0 = 0, nt = CAUSAL ? min((N + TS - 1) / TS, (r0 + kResRows) / TS) : (N + TS - 1) / TS;
+  if constexpr (KSPLIT) {
+    int kt1;
+    key_range(a, kk, nt, kt0, kt1);
+    nt = kt1 - kt0;
+  }
   WsDma dma;
-  dma.init(src);
-  dma.copy(0, N, stages);
-  if (nt > 1) dma.copy(TS, N, stages + STAGE);
+  dma.init(src, kt0 * TS);
+  dma.copy(kt0 * TS, N, stages);
+  if (nt > 1) dma.copy((kt0 + 1) * TS, N, stages + STAGE);
 
   Reader<D, TS> rd;
   const int64_t rv = (int64_t)bh * N;
@@ -233,15 +260,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int ks = 0; ks < NKS; ++ks) {
         const bool more = ks + 1 < NKS;
         if (ks == 0) {
-          S[P] = mfma_vv_first(xk, qf[0]);
+          S[P] = mfma_vv_first<KSPLIT>(xk, qf[0]);
           group(0);
           sched_fence();
-          F[P] = mfma_vv_first(xk, uqf[0]);
+          F[P] = mfma_vv_first<KSPLIT>(xk, uqf[0]);
         } else {
-          mfma_vv(S[P], xk, qf[ks]);
+          mfma_vv<KSPLIT>(S[P], xk, qf[ks]);
           group(5 * ks);
           sched_fence();
-          mfma_vv(F[P], xk, uqf[ks]);
+          mfma_vv<KSPLIT>(F[P], xk, uqf[ks]);
         }
         if (more) {
           bk = stage_ptr(rel, rd.row[ks + 1]);
@@ -250,22 +277,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         group(5 * ks + 1);
         sched_fence();
         if (ks == 0) {
-          DP[P] = mfma_vv_init(xv, df[0], negd);
+          DP[P] = mfma_vv_init<KSPLIT>(xv, df[0], negd);
         } else {
-          mfma_vv(DP[P], xv, df[ks]);
+          mfma_vv<KSPLIT>(DP[P], xv, df[ks]);
         }
         if (more) xv = rd_a(bk, 1);
         group(5 * ks + 2);
         sched_fence();
         if (ks == 0) {
-          C[P] = mfma_vv_first(xuv, df[0]);
+          C[P] = mfma_vv_first<KSPLIT>(xuv, df[0]);
         } else {
-          mfma_vv(C[P], xuv, df[ks]);
+          mfma_vv<KSPLIT>(C[P], xuv, df[ks]);
         }
         if (more) xuv = rd_a(bk, 3);
         group(5 * ks + 3);
         sched_fence();
-        mfma_vv(F[P], xuk, qf[ks]);
+        mfma_vv<KSPLIT>(F[P], xuk, qf[ks]);
         if (more) xuk = rd_a(bk, 2);
         group(5 * ks + 4);
         sched_fence();
@@ -275,7 +302,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // P = 0 through S = -inf.
     auto mask_tile = [&](auto Pc, int t) {
       constexpr int P = decltype(Pc)::value;
-      const int key0 = t * TS;
+      const int key0 = (kt0 + t) * TS;
       if ((key0 + TS > N) || (CAUSAL && key0 + TS - 1 > r0 + wi * 32)) {
 #pragma unroll
         for (int idx = 0; idx < 16; ++idx) {
@@ -315,7 +342,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     auto steady = [&](auto Pc, int sl) {
       constexpr int P = decltype(Pc)::value;
       constexpr std::integral_constant<int, 1 - P> Qc{};
-      if (sl + 2 < nt) dma.copy((sl + 2) * TS, N, stages + stage_off(sl + 2));
+      if (sl + 2 < nt) dma.copy((kt0 + sl + 2) * TS, N, stages + stage_off(sl + 2));
       vfence4(S[1 - P], F[1 - P], DP[1 - P], C[1 - P]);
       mask_tile(Qc, sl - 1);
       float pair[4];
@@ -336,7 +363,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
 
     // Slot 0: scores of tile 0.
-    if (2 < nt) dma.copy(2 * TS, N, stages + 2 * STAGE);
+    if (2 < nt) dma.copy((kt0 + 2) * TS, N, stages + 2 * STAGE);
     scores(std::integral_constant<int, 0>{}, 0, [](int) {});
     end_slot(0);
     int sl = 1;
@@ -360,7 +387,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const float alpha = half_sum(alpha_p);
     const float eo = half_sum(eo_p);
-    if (hh == 0) {
+    if constexpr (KSPLIT) {
+      // Key split: this key range's row sums; the sum kernel does the rest.
+      if (hh == 0 && row < N) {
+        kpart_rowsum(a, kk, 0, bh)[row] = alpha;
+        kpart_rowsum(a, kk, 1, bh)[row] = eo;
+        if (kk == 0) a.D[rv + row] = Di;
+      }
+    } else if (hh == 0) {
       rowx[wi][l] = alpha;
       if (row < N) {
         a.alpha[rv + row] = alpha;
@@ -390,7 +424,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
 
     for (int sl = 0; sl < nt + 2; ++sl) {
-      if (sl + 2 < nt) dma.copy((sl + 2) * TS, N, stages + stage_off(sl + 2));
+      if (sl + 2 < nt) dma.copy((kt0 + sl + 2) * TS, N, stages + stage_off(sl + 2));
       if (sl >= 2) {
         const int kt = sl - 2;
         const uint32_t rel = stage_off(kt);
@@ -439,12 +473,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bf16x8 xv = tr(1, db, s2);
             const bf16x8 xk = tr(0, db, s2);
             const bf16x8 xuk = tr(2, db, s2);
-            mfma_vv(ag[db], xuv, bp);
-            mfma_vv(ag[db], xv, bpf);
-            mfma_vv(aom[db], xk, bpt);
-            mfma_vv(aom[db], xuk, bds);
-            mfma_vv(ar[db], xk, bds);
-            mfma_vv(abk[db], xk, bp);
+            mfma_vv<KSPLIT>(ag[db], xuv, bp);
+            mfma_vv<KSPLIT>(ag[db], xv, bpf);
+            mfma_vv<KSPLIT>(aom[db], xk, bpt);
+            mfma_vv<KSPLIT>(aom[db], xuk, bds);
+            mfma_vv<KSPLIT>(ar[db], xk, bds);
+            mfma_vv<KSPLIT>(abk[db], xk, bp);
           }
         }
       }
@@ -453,8 +487,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vfence4(ag[db], aom[db], ar[db], abk[db]);
     __syncthreads();  // alpha and E° of the producers are in LDS
-    const float alpha = rowx[wi][l & 31];
     const float eob = half_sum(eob_c);
+    if constexpr (KSPLIT) {
+      // Key split: this key range's accumulators and E°_b, raw.
+      if (hh == 0 && row < N) kpart_rowsum(a, kk, 2, bh)[row] = eob;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        store_out(kpart_acc<D>(a, kk, 0, bh), D, row, N, db, [&](int idx) { return ag[db][idx]; });
+        store_out(kpart_acc<D>(a, kk, 1, bh), D, row, N, db, [&](int idx) { return aom[db][idx]; });
+        store_out(kpart_acc<D>(a, kk, 2, bh), D, row, N, db, [&](int idx) { return ar[db][idx]; });
+        store_out(kpart_acc<D>(a, kk, 3, bh), D, row, N, db, [&](int idx) { return abk[db][idx]; });
+      }
+      return;
+    }
+    const float alpha = rowx[wi][l & 31];
     const HeadPtr<float> o = head_of<float>(a.o, bb, hd);
     float* gq = head_out(a.r0, bb, hd);
     float* gdo = head_out(a.r3, bb, hd);

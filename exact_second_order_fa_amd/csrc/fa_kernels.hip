@@ -36,10 +36,12 @@ struct Args {
   float* ps;                           // [B*H][ceil(N/128)][4][128] column-pass chain inits
   float* bs;                           // [B*H][ceil(N/128)][2][128] first-backward column chain inits (or null)
   float* part;                         // key-side partial sums of a split group (or null), see GroupSplit
+  float* kpart;                        // row-pass partial sums of a key split (or null), see KeySplit
   int B, H, N;
   int Hk, G;                 // key/value heads and query heads per key/value head (H = Hk * G)
   int gs, nsplit;            // column kernels: query heads per workgroup and partial sums per key block
   int rs;                    // column kernels: query-row ranges per head subset (nsplit = G / gs * rs)
+  int ks;                    // two-pass row pass: key ranges per row block (1: no key split)
   float tau, pow2, rho, c1;  // c1 = log2(e) * rho
   uint64_t seed;             // dropout: generator key
   uint32_t drop_thr;         // dropout: keep an element iff its byte >= drop_thr (1..255)
@@ -69,6 +71,7 @@ struct Work {
   int bh, b, h, hk, rb;
   int sp;  // column kernels: which partial sum of the key block (0 without a split)
   int rr;  // column kernels: which range of the query rows (0 without a row split)
+  int kk;  // row pass: which range of the keys (0 without a key split)
 };
 
 // heavy_first: causal row-side kernels do work proportional to rb + 1; the
@@ -76,8 +79,11 @@ struct Work {
 // first and the last wave of workgroups is made of the small ones.
 __device__ inline Work work_item(const Args& a, bool heavy_first = false) {
   const int nblk = (a.N + kResRows - 1) / kResRows;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int per = a.B * a.H * nblk;
   Work r;
+  r.kk = w0 / per;  // the key range is the slowest index (0 unless a key split)
+  const int w = w0 - r.kk * per;
   r.bh = w / nblk;
   r.rb = heavy_first ? nblk - 1 - w % nblk : w % nblk;
   r.b = r.bh / a.H;
@@ -154,6 +160,83 @@ __global__ __launch_bounds__(256) void group_sum_kernel(Args a) {
   const TDesc& t = which ? a.r2 : a.r1;
   float* dst = head_out(t, b, hk) + (int64_t)n * t.sn + c;
   *reinterpret_cast<f32x4*>(dst) = acc;
+}
+
+// Key split of the two-pass row pass (KeySplit).  Row-side workgroups are
+// too few to fill the chip when B * H * ceil(N / 128) < 256 (multi-query at
+// N = 2048: 128); then each row block's keys are cut into ks ranges of whole
+// tiles, workgroup kk takes tiles [nt kk / ks, nt (kk + 1) / ks), and instead
+// of the epilogue it stores its raw sums -- alpha, E°, the E° of the
+// bf16-rounded operands, and the four accumulators G, Omega, R', B -- all
+// linear in the keys.  a.kpart holds [ks][3][B*H][N] row sums, then
+// [ks][4][B*H][N][D] accumulators; bob_ksplit_sum_kernel adds them in order.
+__device__ inline void key_range(const Args& a, int kk, int nt, int& t0, int& t1) {
+  t0 = (int)((int64_t)nt * kk / a.ks);
+  t1 = (int)((int64_t)nt * (kk + 1) / a.ks);
+}
+__device__ inline float* kpart_rowsum(const Args& a, int kk, int j, int64_t bh) {
+  return a.kpart + (((int64_t)kk * 3 + j) * a.B * a.H + bh) * a.N;
+}
+template <int D>
+__device__ inline float* kpart_acc(const Args& a, int kk, int m, int64_t bh) {
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  return a.kpart + (int64_t)a.ks * 3 * rows + (((int64_t)kk * 4 + m) * a.B * a.H + bh) * a.N * D;
+}
+
+// The row pass's epilogue over the key-split partial sums, in split order
+// (deterministic): one thread per 4 consecutive floats of a row (rows padded
+// to whole 128-row blocks, whose chain inits it also writes).  Same outputs
+// as the unsplit row pass: gdO = G - alpha O, gQ = tau (Omega - alpha R' -
+// E°_b B), alpha, E = E° - alpha D (D stored by key range 0), and the chain
+// inits -L/rho, -D, -alpha/rho, -E° ((-inf, 0, 0, 0) past N).
+template <int D>
+__global__ __launch_bounds__(256) void bob_ksplit_sum_kernel(Args a) {
+  constexpr int CH = D / 4;
+  const int nblk = (a.N + kPsRows - 1) / kPsRows;
+  const int64_t prow = (int64_t)nblk * kPsRows;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * a.H * prow * CH) return;
+  const int c = (int)(i % CH) * 4;
+  const int64_t rr = i / CH;
+  const int64_t bh = rr / prow;
+  const int row = (int)(rr % prow);
+  const bool ok = row < a.N;
+  float alpha = 0.0f, eo = 0.0f, eob = 0.0f;
+  if (ok) {
+    for (int kk = 0; kk < a.ks; ++kk) {
+      alpha += kpart_rowsum(a, kk, 0, bh)[row];
+      eo += kpart_rowsum(a, kk, 1, bh)[row];
+      eob += kpart_rowsum(a, kk, 2, bh)[row];
+    }
+  }
+  const int64_t rv = bh * a.N;
+  const float Di = ok ? a.D[rv + row] : 0.0f;
+  if (c == 0) {
+    if (ok) {
+      a.alpha[rv + row] = alpha;
+      a.E[rv + row] = eo - alpha * Di;
+    }
+    float* ps = a.ps + (bh * nblk + row / kPsRows) * 4 * kPsRows + row % kPsRows;
+    const float irho = 1.0f / a.rho;
+    ps[0] = ok ? -a.lse[rv + row] * irho : -INFINITY;
+    ps[kPsRows] = ok ? -Di : 0.0f;
+    ps[2 * kPsRows] = ok ? -alpha * irho : 0.0f;
+    ps[3 * kPsRows] = ok ? -eo : 0.0f;
+  }
+  if (!ok) return;
+  f32x4 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    acc[m] = *reinterpret_cast<const f32x4*>(kpart_acc<D>(a, 0, m, bh) + (int64_t)row * D + c);
+    for (int kk = 1; kk < a.ks; ++kk) acc[m] += *reinterpret_cast<const f32x4*>(kpart_acc<D>(a, kk, m, bh) + (int64_t)row * D + c);
+  }
+  const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+  const HeadPtr<float> o = head_of<float>(a.o, b, h);
+  const f32x4 ov = *reinterpret_cast<const f32x4*>(o.p + (int64_t)row * o.sn + c);
+  float* gq = head_out(a.r0, b, h) + (int64_t)row * a.r0.sn + c;
+  float* gdo = head_out(a.r3, b, h) + (int64_t)row * a.r3.sn + c;
+  *reinterpret_cast<f32x4*>(gdo) = acc[0] - alpha * ov;
+  *reinterpret_cast<f32x4*>(gq) = a.tau * (acc[1] - alpha * acc[2] - eob * acc[3]);
 }
 
 // Row scalars of a streamed tile, staged into LDS next to the operand tiles.

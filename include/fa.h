@@ -155,7 +155,10 @@ fa_status fa_bwd(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
 
 /* Workspace bytes fa_bob needs: D, alpha, E, each B*H*N fp32, in that order,
  * then 16 * B*H*ceil(N/128)*128 bytes of per-row chain inits the row pass
- * leaves for the column pass (an internal layout). */
+ * leaves for the column pass (an internal layout).  Problems too small to
+ * give every compute unit a workgroup (fewer than 256 row or column blocks
+ * of 128) add the partial sums of the kernels that are then split over
+ * several workgroups (an internal layout too). */
 size_t fa_bob_workspace_bytes(const fa_problem* p);
 
 /*
@@ -194,20 +197,23 @@ fa_status fa_bob(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
  * (code being captured into a HIP graph, tight serving loops, harnesses that
  * forbid hipMalloc).  Same arguments and results as fa_bob without the
  * workspace: D, alpha, E and the row pass's per-row values live in a static
- * device array of FA_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on
+ * device array of FA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on
  * each GPU it runs on until the process ends, so D, alpha and E are not
  * returned.  Nothing in the array needs clearing: the row pass writes every
  * value the column pass reads.  The array's address on the current device is
  * looked up on the first call made with that device current; call with the
  * stream's device current.
  * Limit: fa_bob_workspace_bytes(p) <= FA_NOALLOC_SCRATCH_BYTES, i.e. about
- * B*H*N <= 1.19 million rows (N = 262,144 with B*H = 4 fits); a larger
- * problem returns FA_ERR_WORKSPACE before anything is launched.
+ * B*H*N <= 2.39 million rows when nothing is split (N = 262,144 with B*H = 8
+ * fits); small problems whose kernels split (see fa_bob_workspace_bytes)
+ * also hold their partial sums there (multi-query, 8 heads, N = 2048, d =
+ * 64: 52 MiB).  A larger problem returns FA_ERR_WORKSPACE before anything is
+ * launched.
  * Calls that overlap on one GPU (on different streams, or from several host
  * threads without ordering) share the array and race: serialise them.
  * Allocates nothing, no torch or library allocator included.
  */
-#define FA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 fa_status fa_bob_noalloc(const fa_problem* p, fa_tensor q, fa_tensor k, fa_tensor v,
                          fa_tensor o, const float* lse, fa_tensor dout,
                          fa_tensor uq, fa_tensor uk, fa_tensor uv,

@@ -40,7 +40,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 10300  # 1.3.0: fa_bob_noalloc (1.2.0: dropout and seed; 1.1.0: H_kv)
+    # 1.4.0: key/row split partials in fa_bob's workspace, 64 MiB no-alloc array
+    # (1.3.0: fa_bob_noalloc; 1.2.0: dropout and seed; 1.1.0: H_kv)
+    assert lib.fa_version() == 10400
     for code in range(8):
         s = lib.fa_status_str(code).decode()
         assert s and s != "unknown status"
@@ -101,15 +103,22 @@ def test_workspace_sizes(lib):
         (_align64(3 * 8 * 8192 + 4 * 8 * 8192) + 2 * 4 * 8192 * 64) * 4
     # Still short of 256 after splitting the group (1 x 1 x 16 key blocks x
     # G = 8 at N = 2048), the non-causal column pass also cuts each query
-    # head's rows into two ranges: 16 partials.  Causal: the group split only.
+    # head's rows into two ranges: 16 partials.  The row pass (8 heads x 16
+    # row blocks = 128 workgroups) cuts each block's keys into two ranges,
+    # whose raw sums follow on a 256-byte boundary: [2][3][B*H][N] row sums
+    # and [2][4][B*H][N][d] accumulators.  Causal: the group split only.
     mqa2k = prob(1, 8, 2048, 64, Hkv=1)
     assert lib.fa_bob_workspace_bytes(ctypes.byref(mqa2k)) == \
-        (_align64(3 * 8 * 2048 + 4 * 8 * 2048) + 2 * 16 * 2048 * 64) * 4
+        (_align64(_align64(3 * 8 * 2048 + 4 * 8 * 2048) + 2 * 16 * 2048 * 64) + 2 * 8 * 2048 * (3 + 4 * 64)) * 4
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 8, 2048, 64, Hkv=1, causal=1))) == \
         (_align64(3 * 8 * 2048 + 4 * 8 * 2048) + 2 * 8 * 2048 * 64) * 4
-    # Multi-head with few blocks (4 heads x 32 blocks = 128): two row ranges.
-    # Ranges keep at least two 128-row blocks, so N = 300 (3 blocks) is never cut.
+    # Multi-head with few blocks (4 heads x 32 blocks = 128): two row ranges
+    # in the column pass, two key ranges in the row pass.  Ranges keep at
+    # least two 128-row blocks, so N = 300 (3 blocks) is never cut.
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 4, 4096, 64))) == \
+        (_align64(_align64(3 * 4 * 4096 + 4 * 4 * 4096) + 2 * 2 * 4 * 4096 * 64) + 2 * 4 * 4096 * (3 + 4 * 64)) * 4
+    # Dropout keeps the row pass whole (its key split is not built).
+    assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 4, 4096, 64, dropout=0.1))) == \
         (_align64(3 * 4 * 4096 + 4 * 4 * 4096) + 2 * 2 * 4 * 4096 * 64) * 4
     assert lib.fa_bob_workspace_bytes(ctypes.byref(prob(1, 1, 300, 64))) == \
         _align64(3 * 300 + 4 * 384) * 4
@@ -265,7 +274,7 @@ def test_noalloc_validation(lib):
     assert noalloc(lib, prob(), bad) == 1
     assert noalloc(lib, prob(d=96)) == 5
     small = prob(B=1, H=4, N=65536)
-    big = prob(B=1, H=8, N=262144)
+    big = prob(B=1, H=16, N=262144)
     assert lib.fa_bob_workspace_bytes(ctypes.byref(small)) <= fa.NOALLOC_SCRATCH_BYTES
     assert lib.fa_bob_workspace_bytes(ctypes.byref(big)) > fa.NOALLOC_SCRATCH_BYTES
     assert noalloc(lib, big) == 6

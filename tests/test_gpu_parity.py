@@ -94,8 +94,12 @@ def test_fp32_shapes(B, H, N):
 
 
 def test_custom_scale_bf16():
-    """A scale that is not a power of two at d = 64 (rho != 1 path)."""
+    """A scale that is not a power of two at d = 64 (rho != 1 path); at
+    N = 700 the row pass also splits each block's keys into two ranges (and
+    the column pass each head's rows), at d = 64 and d = 128."""
     check_case(1, 2, 200, 64, "bf16", 301, scale=0.1)
+    check_case(1, 2, 700, 64, "bf16", 310, scale=0.1)
+    check_case(1, 2, 700, 128, "bf16", 311, scale=0.1)
 
 
 def test_custom_scale_fp32():

@@ -94,7 +94,7 @@ def test_library_assembly_has_no_mfma_hazards(tmp_path):
     # another one); inside, at most four reloads per tile are allowed (the
     # causal row pass reloads three 8-byte values before each tile's copy).
     def allowed(k, n):
-        drop_row_pass = "bob_pass1_dma_kernelILi128ELi64E" in k and k.endswith("ELi0ELb1EEEvNS_4ArgsE")
+        drop_row_pass = "bob_pass1_dma_kernelILi128ELi64E" in k and k.endswith("ELi0ELb1ELb0EEEvNS_4ArgsE")
         drop_dq = "bwd_dq_dma_kernelILi128ELi64E" in k and k.endswith("ELb1EEEvNS_4ArgsE")
         return (drop_row_pass or drop_dq) and n <= 64 and tile_loops_light(kernel_lines(text, k))
 
