@@ -496,8 +496,11 @@ def main():
     progress("hvp step")
     hvp = hvp_leg(r)
     progress("prerequisites")
-    fwd_ms = time_plain(r.fwd, max(3, args.steps // 4))
-    bwd_ms = time_plain(r.bwd, max(3, args.steps // 4))
+    # Like the sweep legs: back to back for SETTLE_MS, then timed over at
+    # least TIMED_MS, so that fa_fwd and fa_bwd are reported at a settled
+    # clock whatever --steps is.
+    fwd_ms = time_plain(r.fwd, reps_for(settle(r.fwd)))
+    bwd_ms = time_plain(r.bwd, reps_for(settle(r.bwd)))
     progress(f"headline: {args.warmup} warm-up and {args.steps} timed steps")
     wall, step_ev, per = time_steps(r, args.steps, args.warmup)
     bob_ms = time_plain(r.bob, args.steps)
