@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(kPsRows % TS == 0 && (TS == 64 || TS == 128), "tiles split the staged scalar blocks");
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
-  const Work wk = work_item_cols(a);
+  const Work wk = work_item_cols(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);

@@ -167,8 +167,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kk = KSPLIT ? wid0 / (a.B * a.H * nblk) : 0;  // key range
   const int wid = wid0 - kk * (a.B * a.H * nblk);
   // Causal: the largest row blocks of a head first (see work_item).
-  const int bh = wid / nblk, rb = CAUSAL ? nblk - 1 - wid % nblk : wid % nblk, bb = bh / a.H, hd = bh % a.H,
-            hk = hd / a.G;
+  int bh, rb;
+  if constexpr (CAUSAL) {
+    int k;
+    longest_first(wid, gridDim.x, nblk, bh, k);
+    rb = nblk - 1 - k;
+  } else {
+    bh = wid / nblk;
+    rb = wid % nblk;
+  }
+  const int bb = bh / a.H, hd = bh % a.H, hk = hd / a.G;
   const int N = a.N;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool producer = wave < 4;

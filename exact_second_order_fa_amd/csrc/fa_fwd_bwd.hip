@@ -353,7 +353,7 @@ bwd_dkdv_dma_kernel(Args a) {
   static_assert(kPsRows % TS == 0 && SBYTES % 512 == 0 && SBYTES <= 1024, "staged inits: one wave-wide copy");
   __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
-  const Work wk = work_item_cols(a);
+  const Work wk = work_item_cols(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);

@@ -75,7 +75,7 @@ struct Work {
 };
 
 // heavy_first: causal row-side kernels do work proportional to rb + 1; the
-// blocks of a head are taken in descending rb so the largest ones start
+// blocks are taken in descending rb (longest_first) so the largest ones start
 // first and the last wave of workgroups is made of the small ones.
 __device__ inline Work work_item(const Args& a, bool heavy_first = false) {
   const int nblk = (a.N + kResRows - 1) / kResRows;
@@ -84,8 +84,14 @@ __device__ inline Work work_item(const Args& a, bool heavy_first = false) {
   Work r;
   r.kk = w0 / per;  // the key range is the slowest index (0 unless a key split)
   const int w = w0 - r.kk * per;
-  r.bh = w / nblk;
-  r.rb = heavy_first ? nblk - 1 - w % nblk : w % nblk;
+  if (heavy_first) {
+    int k;
+    longest_first(w, gridDim.x, nblk, r.bh, k);
+    r.rb = nblk - 1 - k;
+  } else {
+    r.bh = w / nblk;
+    r.rb = w % nblk;
+  }
   r.b = r.bh / a.H;
   r.h = r.bh % a.H;
   r.hk = r.h / a.G;
@@ -97,15 +103,21 @@ __device__ inline Work work_item(const Args& a, bool heavy_first = false) {
 // hk * G + sp * gs .. + gs - 1 and leaves its sums in a.part; the split index
 // is the slowest, so the workgroups streaming the same query heads sit on one
 // XCD.
-__device__ inline Work work_item_cols(const Args& a) {
+// causal: key block rb streams the rows from 128 rb on, so rb = 0 is the
+// longest; without a split the blocks are taken longest first.
+__device__ inline Work work_item_cols(const Args& a, bool causal = false) {
   const int nblk = (a.N + kResRows - 1) / kResRows;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int per = a.B * a.Hk * nblk;
   Work r;
   r.sp = w / per;
   const int w2 = w - r.sp * per;
-  r.bh = w2 / nblk;
-  r.rb = w2 % nblk;
+  if (causal && a.nsplit == 1) {
+    longest_first(w2, gridDim.x, nblk, r.bh, r.rb);
+  } else {
+    r.bh = w2 / nblk;
+    r.rb = w2 % nblk;
+  }
   r.b = r.bh / a.Hk;
   r.hk = r.bh % a.Hk;
   const int sh = r.sp / a.rs;  // subset of the group's query heads
@@ -743,7 +755,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][2 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float scl[2][2 * TS];
 
-  const Work wk = work_item_cols(a);
+  const Work wk = work_item_cols(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);
@@ -1025,7 +1037,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ __attribute__((aligned(16))) T lds[2][3 * S::ELEMS];
   __shared__ __attribute__((aligned(16))) float scl[2][4 * TS];
 
-  const Work wk = work_item_cols(a);
+  const Work wk = work_item_cols(a, CAUSAL);
   const int N = a.N;
   const int l = lane_id(), hh = l >> 5;
   const int col = wk.rb * kResRows + (threadIdx.x >> 6) * 32 + (l & 31);

@@ -124,6 +124,28 @@ __device__ inline int xcd_remap(int g, int total) {
   return (g % 8) * (total / 8) + g / 8;
 }
 
+// Causal work items (after xcd_remap): block k of a head, k = 0 the longest,
+// does work that falls with k.  Head-major order, each head's blocks longest
+// first, keeps the workgroups an XCD runs at once on few heads, whose
+// streamed tiles then hit its L2, but puts the long blocks of its last heads
+// near the end.  With at most 32 blocks per head (N <= 4096: every head's
+// tiles fit the L2 together, and each compute unit runs few workgroups, so
+// the tail weighs most) and whole heads per XCD (its total / 8 items a
+// multiple of nblk), the XCD runs its heads block-major instead -- every
+// head's longest block, then every head's second -- so its last items are
+// the shortest of all its heads.
+__device__ inline void longest_first(int w, int total, int nblk, int& head, int& k) {
+  const int per_xcd = total / 8;
+  if (nblk <= 32 && total % 8 == 0 && per_xcd % nblk == 0) {
+    const int hx = per_xcd / nblk, x = w / per_xcd, i = w - x * per_xcd;
+    head = x * hx + i % hx;
+    k = i / hx;
+  } else {
+    head = w / nblk;
+    k = w % nblk;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LDS layout of one staged tensor: row copy [TS][D + VEC], transposed copy
 // [D][TS + VEC] (the pad keeps 16-byte alignment and spreads banks).
