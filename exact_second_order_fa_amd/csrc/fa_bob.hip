@@ -627,9 +627,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // and C' = g (dO U_V^T) - alpha D - E, so these two chains start at 0 and take
 // their staged scalars after the mask; W = P g h.  The mask of each pair of
 // sub-tiles comes from one shared generator call per lane (DropCol).
-template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL, bool DROP = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bob_pass2_dma_kernel(Args a) {
+// TWO: two waves per SIMD (two workgroups per CU, 256 registers a wave), for
+// the split schedule at d = 64 without causality or dropout; the launch uses
+// it only for grids of whole multiples of 512 workgroups.
+template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL, bool DROP = false, bool TWO = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TWO ? 2 : 1, TWO ? 2 : 1))) void
+bob_pass2_dma_kernel(Args a) {
   static_assert(!DROP || (SPLIT && TS % 64 == 0), "dropout runs the split schedule on pairs of sub-tiles");
+  static_assert(!TWO || (D == 64 && SPLIT && !CAUSAL && !DROP), "the two-wave instance is the d = 64 split schedule");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int NSLICE = 2 * NDB;
