@@ -387,10 +387,10 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
       }
     }
     if (want(col_phase)) {
-      // d = 64 without causality: two workgroups per CU (64-row tiles, split
-      // schedule) when the grid fills every CU's two slots evenly.
-      const bool two = D == 64 && !C && gc.x % 512 == 0;
-      if constexpr (D == 64 && !C) {
+      // d = 64: two workgroups per CU (64-row tiles, split schedule) when the
+      // grid fills every CU's two slots evenly.
+      const bool two = D == 64 && gc.x % 512 == 0;
+      if constexpr (D == 64) {
         if (two)
           hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C, false, true>), gc, b, 0, st, a);
       }

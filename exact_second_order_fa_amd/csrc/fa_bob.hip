@@ -628,13 +628,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // their staged scalars after the mask; W = P g h.  The mask of each pair of
 // sub-tiles comes from one shared generator call per lane (DropCol).
 // TWO: two waves per SIMD (two workgroups per CU, 256 registers a wave), for
-// the split schedule at d = 64 without causality or dropout; the launch uses
-// it only for grids of whole multiples of 512 workgroups.
+// the split schedule at d = 64 without dropout; the launch uses it only for
+// grids of whole multiples of 512 workgroups.
 template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL, bool DROP = false, bool TWO = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TWO ? 2 : 1, TWO ? 2 : 1))) void
 bob_pass2_dma_kernel(Args a) {
   static_assert(!DROP || (SPLIT && TS % 64 == 0), "dropout runs the split schedule on pairs of sub-tiles");
-  static_assert(!TWO || (D == 64 && SPLIT && !CAUSAL && !DROP), "the two-wave instance is the d = 64 split schedule");
+  static_assert(!TWO || (D == 64 && SPLIT && !DROP), "the two-wave instance is the d = 64 split schedule");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int NSLICE = 2 * NDB;
@@ -744,9 +744,17 @@ bob_pass2_dma_kernel(Args a) {
         const bf16x8 xq = rd_row<D, TS>(tq, rd, sub, ks);
         const bf16x8 xuq = rd_row<D, TS>(tuq, rd, sub, ks);
         const bf16x8 xd = rd_row<D, TS>(tdo, rd, sub, ks);
-        mfma_v(s, xq, kf[ks]);
-        mfma_v(f, xuq, kf[ks]);
-        mfma_v(f, xq, ukf[ks]);
+        // The causal two-wave instance, short of registers, copies K and U_K
+        // back from AGPRs right before these: its MFMAs carry the wait.
+        if constexpr (TWO && CAUSAL) {
+          mfma_v_w(s, xq, kf[ks]);
+          mfma_v_w(f, xuq, kf[ks]);
+          mfma_v_w(f, xq, ukf[ks]);
+        } else {
+          mfma_v(s, xq, kf[ks]);
+          mfma_v(f, xuq, kf[ks]);
+          mfma_v(f, xq, ukf[ks]);
+        }
         if (DROP && ks == 0) {
           dp = RESA ? mfma_first_a(xd, vf[0]) : mfma_first(xd, vf[0]);
           c = RESA ? mfma_first_a(xd, uvf[0]) : mfma_first(xd, uvf[0]);
