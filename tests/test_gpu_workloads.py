@@ -67,6 +67,42 @@ def test_mid_workload_full():
         assert e <= TOL["bf16"], key
 
 
+# ------------------------------------------------- two-wave column pass
+# d = 64 grids of a whole multiple of 512 column workgroups run the column
+# pass at two waves per SIMD (64-row tiles).  The workloads reach it only at
+# N a multiple of 128 with one query head per key/value head; these cases,
+# 2 x 8 x 32 = 512 column blocks each, add a ragged last tile (N = 4000,
+# also causal) and two query heads per key/value head (its head loop).
+# Every element of every output against the streaming oracle.
+
+
+def _two_wave_case(H, Hkv, N, causal, seed):
+    from fa_inputs import make_inputs
+    from oracle import bob_streaming_gqa
+
+    say(f"two-wave column pass: B=2 H={H} H_kv={Hkv} N={N} d=64 causal={causal} seed={seed}")
+    raw, f64 = make_inputs(2, H, N, 64, seed, "bf16", H_kv=Hkv)
+    got = run_path(to_device(raw, "bf16"), causal=causal)
+    args = (*(f64[n] for n in NAMES), 1.0 / 8.0)
+    if Hkv == H:
+        ref = bob_streaming(*args, threads=oracle_threads(), causal=causal)
+    else:
+        ref = bob_streaming_gqa(*args, threads=oracle_threads(), causal=causal)
+    for key in ALL_KEYS:
+        e = rel(host(got[key]), ref[key])
+        say(f"  {key} {e:.2e}")
+        assert e <= TOL["bf16"], key
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_wave_column_pass_ragged(causal):
+    _two_wave_case(8, 8, 4000, causal, 511 + int(causal))
+
+
+def test_two_wave_column_pass_grouped_heads():
+    _two_wave_case(16, 8, 4096, False, 513)
+
+
 # --------------------------------------------------------------- whole tensors
 
 _RUN = {}
