@@ -138,9 +138,13 @@ def test_rising_scores_move_the_reference_maximum(causal):
 
 
 def test_strided_layout():
-    """Inputs and outputs stored [B, N, H, d] (non-contiguous head stride)."""
+    """Inputs and outputs stored [B, N, H, d] (non-contiguous head stride); at
+    N = 700 the row pass's key split and the column pass's row split write
+    their results through the same strides."""
     check_case(2, 3, 150, 64, "bf16", 305, layout="bnhd")
     check_case(1, 2, 90, 128, "bf16", 306, layout="bnhd")
+    check_case(1, 2, 700, 64, "bf16", 312, layout="bnhd")
+    check_case(1, 2, 700, 128, "bf16", 313, layout="bnhd")
 
 
 def test_deterministic():
