@@ -387,17 +387,16 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
       }
     }
     if (want(col_phase)) {
-      // d = 64: two workgroups per CU (64-row tiles, split schedule) when the
-      // grid fills every CU's two slots evenly.
-      const bool two = D == 64 && gc.x % 512 == 0;
       if constexpr (D == 64) {
-        if (two)
+        // Two workgroups per CU (64-row tiles, split schedule) when the grid
+        // fills every CU's two slots evenly, else the woven one-wave kernel.
+        if (gc.x % 512 == 0)
           hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C, false, true>), gc, b, 0, st, a);
-      }
-      if constexpr (D == 64) {
-        if (!two) hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), gc, b, 0, st, a);
-      } else
+        else
+          hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, false, false, C>), gc, b, 0, st, a);
+      } else {
         hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C>), gc, b, 0, st, a);
+      }
       launch_group_sum<D>(c, a, st);
     }
   } else {
