@@ -76,13 +76,13 @@ def test_mid_workload_full():
 # Every element of every output against the streaming oracle.
 
 
-def _two_wave_case(H, Hkv, N, causal, seed):
+def _two_wave_case(H, Hkv, N, causal, seed, schedule=None):
     from fa_inputs import make_inputs
     from oracle import bob_streaming_gqa
 
-    say(f"two-wave column pass: B=2 H={H} H_kv={Hkv} N={N} d=64 causal={causal} seed={seed}")
+    say(f"two-wave column pass: B=2 H={H} H_kv={Hkv} N={N} d=64 causal={causal} seed={seed} schedule={schedule}")
     raw, f64 = make_inputs(2, H, N, 64, seed, "bf16", H_kv=Hkv)
-    got = run_path(to_device(raw, "bf16"), causal=causal)
+    got = run_path(to_device(raw, "bf16"), causal=causal, schedule=schedule)
     args = (*(f64[n] for n in NAMES), 1.0 / 8.0)
     if Hkv == H:
         ref = bob_streaming(*args, threads=oracle_threads(), causal=causal)
@@ -101,6 +101,12 @@ def test_two_wave_column_pass_ragged(causal):
 
 def test_two_wave_column_pass_grouped_heads():
     _two_wave_case(16, 8, 4096, False, 513)
+
+
+def test_two_wave_column_pass_after_the_three_pass_row_sweeps():
+    """The three-pass schedule (alpha sweep, row pass with alpha known) hands
+    its chain inits to the same two-wave column pass."""
+    _two_wave_case(8, 8, 4000, False, 514, schedule=2)
 
 
 # --------------------------------------------------------------- whole tensors
