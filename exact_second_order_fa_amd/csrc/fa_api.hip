@@ -288,8 +288,11 @@ void launch_bwd(const Ctx& c, const Args& a, hipStream_t st) {
     }
   }
   if constexpr (sizeof(T) == 2) {
-    // Row scalars D plus the staged chain inits (-L/rho, -D) of the column kernel.
-    hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c, true)), dim3(256), 0, st, a);
+    // Row scalars D plus the staged chain inits (-L/rho, -D) of the column
+    // kernel: at d = 64 from the dQ kernel (which the column kernel follows),
+    // at d = 128 from the row-scalar kernel.
+    if constexpr (D != 64)
+      hipLaunchKernelGGL((fa::rowscalar_kernel<T, D>), dim3(grid_rowscalar(c, true)), dim3(256), 0, st, a);
     constexpr int TS = D == 64 ? 128 : 64;
     const dim3 gc(grid_cols(c) * a.nsplit);
     if (c.drop) {

@@ -229,11 +229,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   bf16x8 qf[NKS], df[NKS];
   load_resident<bf16, D>(qf, q.p, q.sn, row, N, a.pow2);
   load_resident<bf16, D>(df, dout.p, dout.sn, row, N, 1.0f);
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qf[ks]), "+a"(df[ks]));
   const int64_t rv = (int64_t)wk.bh * N;
   const float Li = row < N ? a.lse[rv + row] : 0.0f;
-  const float Di = row < N ? a.D[rv + row] : 0.0f;
+  // d = 64: D = rowsum(dO * O) from the resident dO rows (no row-scalar
+  // kernel); this kernel also stages the dK/dV kernel's chain inits of its
+  // rows, -L/rho and -D ((-inf, 0) on the padding rows of the last block),
+  // which that kernel, launched after it, reads.  d = 128 reads them from the
+  // row-scalar kernel (with its registers it would spill in the dropout
+  // instance, measured 14 % slower there and no faster without dropout).
+  constexpr bool OWN_D = D == 64;
+  const float Di = OWN_D ? resident_rowdot<D>(df, head_of<float>(a.o, wk.b, wk.h), row, N)
+                         : (row < N ? a.D[rv + row] : 0.0f);
+  if (OWN_D && hh == 0) {
+    const bool ok = row < N;
+    if (ok) a.D[rv + row] = Di;
+    const int nblk = (N + kPsRows - 1) / kPsRows;
+    float* st = a.bs + ((int64_t)wk.bh * nblk + row / kPsRows) * 2 * kPsRows + row % kPsRows;
+    st[0] = ok ? -Li / a.rho : -INFINITY;
+    st[kPsRows] = ok ? -Di : 0.0f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+a"(qf[ks]), "+a"(df[ks]));
   const float nl2 = -Li * kLog2e;
   // At d = 64 without dropout the dP chains start from -D (the MFMA's C
   // operand), so dP - D comes out of the matrix core (fa_bwd 2-3 % faster;

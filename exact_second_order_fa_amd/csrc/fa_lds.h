@@ -195,4 +195,28 @@ __device__ inline bf16x8 rd_tr(const char* tile, const Reader<D, TS>& rd, int su
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// D_i = rowsum(dO * O)_i ([FA2-recompute]) of this lane's resident row, from
+// its resident bf16 dO operands (k-step ks holds d-columns 16 ks + 8 hh ..
+// + 7) and the matching fp32 O values; the two halves of the wave hold the
+// two halves of the row.
+template <int D>
+__device__ inline float resident_rowdot(const bf16x8 (&df)[D / 16], const HeadPtr<float>& o, int row, int N) {
+  const int hh = lane_id() >> 5;
+  float acc = 0.0f;
+  if (row < N) {
+    const float* orow = o.p + (int64_t)row * o.sn + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(orow + 16 * ks);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(orow + 16 * ks + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf((float)df[ks][e], x0[e], acc);
+        acc = fmaf((float)df[ks][e + 4], x1[e], acc);
+      }
+    }
+  }
+  return half_sum(acc);
+}
+
 }  // namespace fa
