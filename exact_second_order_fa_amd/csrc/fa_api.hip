@@ -328,7 +328,9 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
   if (c.drop) {  // two-pass schedule (schedule 2 is refused earlier)
     if constexpr (sizeof(T) == 2) {
       // bf16: the LDS-DMA row pass (which computes D itself) and the column
-      // pass's split schedule, both with the mask.
+      // pass's split schedule, both with the mask; at d = 64 without the
+      // causal mask the column pass runs two waves per SIMD when the grid
+      // gives every CU its two workgroups.
       if (want(1)) {
         if constexpr (D == 64)
           hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 128, RHO1, false, C, 0, true>), g, b, 0, st, a);
@@ -336,9 +338,12 @@ void launch_bob(const Ctx& c, const Args& a, hipStream_t st, int schedule, int p
           hipLaunchKernelGGL((fa::bob_pass1_dma_kernel<D, 64, RHO1, true, C, 0, true>), g, b, 0, st, a);
       }
       if (want(2)) {
-        if constexpr (D == 64)
-          hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, true, false, C, true>), gc, b, 0, st, a);
-        else
+        if constexpr (D == 64) {
+          if (!C && gc.x % 512 == 0)
+            hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, false, true, true>), gc, b, 0, st, a);
+          else
+            hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 128, RHO1, true, false, C, true>), gc, b, 0, st, a);
+        } else
           hipLaunchKernelGGL((fa::bob_pass2_dma_kernel<D, 64, RHO1, true, true, C, true>), gc, b, 0, st, a);
         launch_group_sum<D>(c, a, st);
       }

@@ -604,13 +604,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // their staged scalars after the mask; W = P g h.  The mask of each pair of
 // sub-tiles comes from one shared generator call per lane (DropCol).
 // TWO: two waves per SIMD (two workgroups per CU, 256 registers a wave), for
-// the split schedule at d = 64 without dropout; the launch uses it only for
-// grids of whole multiples of 512 workgroups.
+// the split schedule at d = 64 (with dropout only without the causal mask);
+// the launch uses it only for grids of whole multiples of 512 workgroups.
 template <int D, int TS, bool RHO1, bool SPLIT, bool RESA, bool CAUSAL, bool DROP = false, bool TWO = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TWO ? 2 : 1, TWO ? 2 : 1))) void
 bob_pass2_dma_kernel(Args a) {
   static_assert(!DROP || (SPLIT && TS % 64 == 0), "dropout runs the split schedule on pairs of sub-tiles");
-  static_assert(!TWO || (D == 64 && SPLIT && !DROP), "the two-wave instance is the d = 64 split schedule");
+  static_assert(!TWO || (D == 64 && SPLIT && !(DROP && CAUSAL)), "the two-wave instance is the d = 64 split schedule");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
   constexpr int NSLICE = 2 * NDB;
@@ -722,7 +722,7 @@ bob_pass2_dma_kernel(Args a) {
         const bf16x8 xd = rd_row<D, TS>(tdo, rd, sub, ks);
         // The causal two-wave instance, short of registers, copies K and U_K
         // back from AGPRs right before these: its MFMAs carry the wait.
-        if constexpr (TWO && CAUSAL) {
+        if constexpr (TWO && (CAUSAL || DROP)) {
           mfma_v_w(s, xq, kf[ks]);
           mfma_v_w(f, xuq, kf[ks]);
           mfma_v_w(f, xq, ukf[ks]);
@@ -752,20 +752,27 @@ bob_pass2_dma_kernel(Args a) {
       mfma_acc(ak[db], xuq, cds.f[s2]);
       mfma_acc(av[db], xd, cw.f[s2]);
     };
-    // With DROP, nd and nc hold the staged -D and -(alpha D + E) of the
-    // sub-tile's rows and dm its mask.
+    // With DROP, dm holds the mask of the sub-tile pair and the part's four
+    // staged -D and -(alpha D + E) are read from the tile's chain inits here
+    // (one 16-byte LDS read each), not held for the whole sub-tile.
     auto elementwise = [&](int part, const f32x16& s, const f32x16& f, const f32x16& dp, const f32x16& c,
-                           Chain<bf16>& cdt, Chain<bf16>& cds, Chain<bf16>& cw, const f32x16& nd,
-                           const f32x16& nc, const DropCol<2>& dm, int gsub) {
+                           Chain<bf16>& cdt, Chain<bf16>& cds, Chain<bf16>& cw, int sub,
+                           const DropCol<2>& dm) {
+      f32x4 nd, nc;
+      if constexpr (DROP) {
+        const int o = sub * 32 + sig(8 * part + 4 * hh);
+        nd = *reinterpret_cast<const f32x4*>(sc + TS + o);
+        nc = *reinterpret_cast<const f32x4*>(sc + 3 * TS + o);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int idx = 4 * part + e;
         const float p = __builtin_amdgcn_exp2f(s[idx] * a.c1);
         const float h = RHO1 ? f[idx] : f[idx] * a.rho;
         if constexpr (DROP) {
-          const float g = dm.at(a, gsub, idx);
-          const float dpx = fmaf(g, dp[idx], nd[idx]);
-          cdt.f[idx >> 3][idx & 7] = (bf16)(p * fmaf(h, dpx, fmaf(g, c[idx], nc[idx])));
+          const float g = dm.at(a, sub & 1, idx);
+          const float dpx = fmaf(g, dp[idx], nd[e]);
+          cdt.f[idx >> 3][idx & 7] = (bf16)(p * fmaf(h, dpx, fmaf(g, c[idx], nc[e])));
           cds.f[idx >> 3][idx & 7] = (bf16)(p * dpx);
           cw.f[idx >> 3][idx & 7] = (bf16)(p * g * h);
           continue;
@@ -983,17 +990,14 @@ bob_pass2_dma_kernel(Args a) {
     DropCol<2> dm;
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
-      f32x16 nd, nc;
       if constexpr (DROP) {
         if (sub % 2 == 0) dm.init(a, (int64_t)wk.b * a.H + wk.h + gq, t * TS + sub * 32, col);
-        nd = row_init<TS>(sc + TS, sub);
-        nc = row_init<TS>(sc + 3 * TS, sub);
       }
       mfma_fence(s, f, dp, c);
       Chain<bf16> cdt, cds, cw;
 #pragma unroll
       for (int part = 0; part < 4; ++part) {
-        elementwise(part, s, f, dp, c, cdt, cds, cw, nd, nc, dm, sub & 1);
+        elementwise(part, s, f, dp, c, cdt, cds, cw, sub, dm);
         if constexpr (SPLIT) {
           constexpr int H = NDB / 2;
           if (part < 2) {

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import make_inputs
-from oracle import bob_dropout_heads
+from oracle import bob_dropout, bob_dropout_heads, dropout_mask
 from tests.gpu_helpers import host, rel, run_dropout, say, to_device
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +40,35 @@ def test_dropout_parity(B, H, Hkv, N, d, dtype, p, causal):
     say("  " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("H,Hkv", [(16, 16), (32, 16)])
+def test_dropout_two_wave_column_pass(H, Hkv):
+    """d = 64 grids of a whole multiple of 512 column workgroups run the
+    dropout column pass at two waves per SIMD (64-row tiles): 16 key/value
+    heads of 32 ragged key blocks (N = 4000), with one and with two query
+    heads per key/value head.  Every head runs on the GPU; the first and the
+    last key/value head, with all their query heads, are compared element by
+    element (the oracle's mask draw is what bounds the count)."""
+    B, N, d, p = 1, 4000, 64, 0.2
+    seed = 4242 + H
+    say(f"dropout two-wave column pass: B={B} H={H} H_kv={Hkv} N={N} d={d} p={p} seed={seed}")
+    raw, f64 = make_inputs(B, H, N, d, seed, "bf16", H_kv=Hkv)
+    got = {k: host(v) for k, v in run_dropout(to_device(raw, "bf16"), p, seed, False).items()}
+    G = H // Hkv
+    for hk in (0, Hkv - 1):
+        col = {}
+        for h in range(hk * G, (hk + 1) * G):
+            r = bob_dropout(f64["q"][0, h], f64["k"][0, hk], f64["v"][0, hk], f64["do"][0, h], f64["uq"][0, h],
+                            f64["uk"][0, hk], f64["uv"][0, hk], 1.0 / np.sqrt(d), dropout_mask(h, N, p, seed), False)
+            errs = {k: rel(got[k][0, h], r[k]) for k in ("O", "L", "D", "alpha", "E", "gQ", "gdO", "dQ")}
+            say(f"  head {h}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+            assert all(v <= TOL["bf16"] for v in errs.values()), errs
+            for k in ("gK", "gV", "dK", "dV"):
+                col[k] = col.get(k, 0.0) + r[k]
+        errs = {k: rel(got[k][0, hk], col[k]) for k in col}
+        say(f"  key/value head {hk}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+        assert all(v <= TOL["bf16"] for v in errs.values()), errs
 
 
 def test_dropout_rate_rounding_to_zero_is_the_dropout_free_path():
