@@ -413,6 +413,25 @@ def ablation(names, reps=5):
     return out
 
 
+# Sweep workloads whose line also times the prerequisites (fa_fwd, fa_bwd).
+PREREQ_SWEEP = ("long", "hd128", "gpt2c_16k")
+
+
+def prerequisites(r, w):
+    """fa_fwd and fa_bwd on the runner's workload: back to back for SETTLE_MS,
+    then timed over at least TIMED_MS, so that both are reported at a settled
+    clock.  Flops ([FlashBoB] section 3): 2 N^2 d per contraction; forward 2
+    contractions, first backward 5 (S, dP, dV, dQ, dK); causal half."""
+    fwd_ms = time_plain(r.fwd, reps_for(settle(r.fwd)))
+    bwd_ms = time_plain(r.bwd, reps_for(settle(r.bwd)))
+    cf = (0.5 if w.causal else 1.0) * 2.0 * w.B * w.H * w.N * w.N * w.d
+    out = {}
+    for op, ms, n in (("fa_fwd", fwd_ms, 2), ("fa_bwd", bwd_ms, 5)):
+        tf = n * cf / (ms * 1e9)
+        out[op] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_peak": round(tf / peak_of(w), 4)}
+    return out
+
+
 def sweep_leg(name):
     import torch
 
@@ -432,6 +451,8 @@ def sweep_leg(name):
            "device_bytes": device_bytes(r)}
     if 0 in s_per:
         res["rowscalar_ms"] = round(s_per[0], 4)
+    if name in PREREQ_SWEEP:
+        res["prerequisites"] = prerequisites(r, sw)
     if name in PAGES_MS:
         res["pages_ms_context"] = PAGES_MS[name]
     del r
@@ -496,22 +517,11 @@ def main():
     progress("hvp step")
     hvp = hvp_leg(r)
     progress("prerequisites")
-    # Like the sweep legs: back to back for SETTLE_MS, then timed over at
-    # least TIMED_MS, so that fa_fwd and fa_bwd are reported at a settled
-    # clock whatever --steps is.
-    fwd_ms = time_plain(r.fwd, reps_for(settle(r.fwd)))
-    bwd_ms = time_plain(r.bwd, reps_for(settle(r.bwd)))
+    prereq = prerequisites(r, w)
     progress(f"headline: {args.warmup} warm-up and {args.steps} timed steps")
     wall, step_ev, per = time_steps(r, args.steps, args.warmup)
     bob_ms = time_plain(r.bob, args.steps)
     dev_bytes = device_bytes(r)
-    # Prerequisites ([FlashBoB] section 3): 2 N^2 d flops per contraction;
-    # forward 2 contractions, first backward 5 (S, dP, dV, dQ, dK); causal half.
-    cf = (0.5 if w.causal else 1.0) * 2.0 * w.B * w.H * w.N * w.N * w.d
-    prereq = {"fa_fwd": {"ms": round(fwd_ms, 4), "tflops": round(2 * cf / (fwd_ms * 1e9), 1),
-                         "frac_peak": round(2 * cf / (fwd_ms * 1e9) / peak_of(w), 4)},
-              "fa_bwd": {"ms": round(bwd_ms, 4), "tflops": round(5 * cf / (bwd_ms * 1e9), 1),
-                         "frac_peak": round(5 * cf / (bwd_ms * 1e9) / peak_of(w), 4)}}
     flops = w.bob_flops
     peak = peak_of(w)
     value = flops / (wall * 1e9)
@@ -543,7 +553,7 @@ def main():
                                    else "portable") + ", mask from Philox4x64-10"}
 
     kernels_ms = {"bob_pass1": round(per[1], 4), "bob_pass2": round(per[2], 4), "step_events": round(step_ev, 4),
-                  "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": round(fwd_ms, 4)}
+                  "fa_bob_single_call": round(bob_ms, 4), "fa_fwd": prereq["fa_fwd"]["ms"]}
     if 0 in per:
         kernels_ms["rowscalar"] = round(per[0], 4)
     else:

@@ -50,12 +50,14 @@ __device__ inline f32x16 mfma_init_a(bf16x8 a, bf16x8 b, const f32x16& c) {
 // (P g) V while the row sum and L keep P.  The mask of each pair of sub-tiles
 // comes from one shared generator call per lane (DropRow), issued behind the
 // score MFMAs of the next sub-tile.
+// WPE: waves per SIMD (2; 3 for the d = 64 instance with 64-key tiles, 122
+// registers and 33 KB of LDS a workgroup, three workgroups per CU).
 // Largest partial row sum (16 exponentials of one lane) accepted against a
 // stale reference maximum; it bounds every exponential by 2^16.
 constexpr float kLazyBound = 65536.0f;
 
-template <int D, int TS, bool CAUSAL, bool DROP = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_dma_kernel(Args a) {
+template <int D, int TS, bool CAUSAL, bool DROP = false, int WPE = 2>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd_dma_kernel(Args a) {
   static_assert(!DROP || TS % 64 == 0, "the mask comes in pairs of sub-tiles");
   typedef SwTile<D, TS> W;
   constexpr int NKS = D / 16, NDB = D / 32, NSUB = TS / 32;
