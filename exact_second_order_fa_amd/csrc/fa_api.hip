@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "fa.h"
 #include "fa_kernels.hip"
@@ -260,23 +261,24 @@ struct Tiles {
 template <typename T, int D, bool C>
 void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    if (c.drop)
-      hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C, true>), dim3(grid_rows(c)),
-                         dim3(fa::kThreads), 0, st, a);
-    else {
-      // d = 64 at three waves per SIMD (64-key tiles) on grids of at least
-      // two full rounds of three workgroups per CU; below that the CUs of a
-      // last partial round would sit idle longer than the third wave gains.
+    // d = 64 at three waves per SIMD (64-key tiles) on grids of at least two
+    // full rounds of three workgroups per CU; below that the CUs of a last
+    // partial round would sit idle longer than the third wave gains.
+    auto go = [&](auto drop_c) {
+      constexpr bool DR = decltype(drop_c)::value;
       if constexpr (D == 64) {
         if (grid_rows(c) >= 1536) {
-          hipLaunchKernelGGL((fa::fwd_dma_kernel<D, 64, C, false, 3>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st,
-                             a);
+          hipLaunchKernelGGL((fa::fwd_dma_kernel<D, 64, C, DR, 3>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
           return;
         }
       }
-      hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
-                         st, a);
-    }
+      hipLaunchKernelGGL((fa::fwd_dma_kernel<D, D == 64 ? 128 : 64, C, DR>), dim3(grid_rows(c)), dim3(fa::kThreads),
+                         0, st, a);
+    };
+    if (c.drop)
+      go(std::true_type{});
+    else
+      go(std::false_type{});
   } else if (c.drop)
     hipLaunchKernelGGL((fa::fwd_kernel<T, D, Tiles<T, D>::TS, C, true>), dim3(grid_rows(c)), dim3(fa::kThreads), 0,
                        st, a);

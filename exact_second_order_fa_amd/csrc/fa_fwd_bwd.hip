@@ -50,8 +50,9 @@ __device__ inline f32x16 mfma_init_a(bf16x8 a, bf16x8 b, const f32x16& c) {
 // (P g) V while the row sum and L keep P.  The mask of each pair of sub-tiles
 // comes from one shared generator call per lane (DropRow), issued behind the
 // score MFMAs of the next sub-tile.
-// WPE: waves per SIMD (2; 3 for the d = 64 instance with 64-key tiles, 122
-// registers and 33 KB of LDS a workgroup, three workgroups per CU).
+// WPE: waves per SIMD (2; 3 for the d = 64 instances with 64-key tiles, 122
+// registers, 162 with the mask, and 33 KB of LDS a workgroup: three
+// workgroups per CU).
 // Largest partial row sum (16 exponentials of one lane) accepted against a
 // stale reference maximum; it bounds every exponential by 2^16.
 constexpr float kLazyBound = 65536.0f;

@@ -42,25 +42,22 @@ def test_dropout_parity(B, H, Hkv, N, d, dtype, p, causal):
     assert not bad, bad
 
 
-@pytest.mark.parametrize("H,Hkv", [(16, 16), (32, 16)])
-def test_dropout_two_wave_column_pass(H, Hkv):
-    """d = 64 grids of a whole multiple of 512 column workgroups run the
-    dropout column pass at two waves per SIMD (64-row tiles): 16 key/value
-    heads of 32 ragged key blocks (N = 4000), with one and with two query
-    heads per key/value head.  Every head runs on the GPU; the first and the
-    last key/value head, with all their query heads, are compared element by
-    element (the oracle's mask draw is what bounds the count)."""
-    B, N, d, p = 1, 4000, 64, 0.2
-    seed = 4242 + H
-    say(f"dropout two-wave column pass: B={B} H={H} H_kv={Hkv} N={N} d={d} p={p} seed={seed}")
+def _dropout_edge_heads(H, Hkv, p, seed, causal, what):
+    """Every head of B = 1, N = 4000 (32 ragged 128-row blocks), d = 64 runs on
+    the GPU; the first and the last key/value head, with all their query
+    heads, are compared element by element with the dropout oracle (its mask
+    draw is what bounds the count)."""
+    B, N, d = 1, 4000, 64
+    say(f"dropout {what}: B={B} H={H} H_kv={Hkv} N={N} d={d} p={p} causal={causal} seed={seed}")
     raw, f64 = make_inputs(B, H, N, d, seed, "bf16", H_kv=Hkv)
-    got = {k: host(v) for k, v in run_dropout(to_device(raw, "bf16"), p, seed, False).items()}
+    got = {k: host(v) for k, v in run_dropout(to_device(raw, "bf16"), p, seed, causal).items()}
     G = H // Hkv
     for hk in (0, Hkv - 1):
         col = {}
         for h in range(hk * G, (hk + 1) * G):
             r = bob_dropout(f64["q"][0, h], f64["k"][0, hk], f64["v"][0, hk], f64["do"][0, h], f64["uq"][0, h],
-                            f64["uk"][0, hk], f64["uv"][0, hk], 1.0 / np.sqrt(d), dropout_mask(h, N, p, seed), False)
+                            f64["uk"][0, hk], f64["uv"][0, hk], 1.0 / np.sqrt(d), dropout_mask(h, N, p, seed),
+                            causal)
             errs = {k: rel(got[k][0, h], r[k]) for k in ("O", "L", "D", "alpha", "E", "gQ", "gdO", "dQ")}
             say(f"  head {h}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
             assert all(v <= TOL["bf16"] for v in errs.values()), errs
@@ -69,6 +66,21 @@ def test_dropout_two_wave_column_pass(H, Hkv):
         errs = {k: rel(got[k][0, hk], col[k]) for k in col}
         say(f"  key/value head {hk}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
         assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("H,Hkv", [(16, 16), (32, 16)])
+def test_dropout_two_wave_column_pass(H, Hkv):
+    """d = 64 grids of a whole multiple of 512 column workgroups run the
+    dropout column pass at two waves per SIMD (64-row tiles): 16 key/value
+    heads, with one and with two query heads per key/value head."""
+    _dropout_edge_heads(H, Hkv, 0.2, 4242 + H, False, "two-wave column pass")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_three_wave_forward(causal):
+    """d = 64 grids of at least 1536 row workgroups (48 heads here) run the
+    dropout forward at three waves per SIMD with 64-key tiles."""
+    _dropout_edge_heads(48, 48, 0.15, 4300 + int(causal), causal, "three-wave forward")
 
 
 def test_dropout_rate_rounding_to_zero_is_the_dropout_free_path():
