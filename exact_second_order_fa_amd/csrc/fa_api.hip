@@ -261,14 +261,20 @@ struct Tiles {
 template <typename T, int D, bool C>
 void launch_fwd(const Ctx& c, const Args& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    // d = 64 at three waves per SIMD (64-key tiles) on grids of at least two
-    // full rounds of three workgroups per CU; below that the CUs of a last
-    // partial round would sit idle longer than the third wave gains.
+    // Three waves per SIMD (64-key tiles at d = 64, 32-key tiles at d = 128
+    // without dropout) on grids of at least two full rounds of three
+    // workgroups per CU; below that the CUs of a last partial round would sit
+    // idle longer than the third wave gains.
     auto go = [&](auto drop_c) {
       constexpr bool DR = decltype(drop_c)::value;
       if constexpr (D == 64) {
         if (grid_rows(c) >= 1536) {
           hipLaunchKernelGGL((fa::fwd_dma_kernel<D, 64, C, DR, 3>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
+          return;
+        }
+      } else if constexpr (!DR) {
+        if (grid_rows(c) >= 1536) {
+          hipLaunchKernelGGL((fa::fwd_dma_kernel<D, 32, C, DR, 3>), dim3(grid_rows(c)), dim3(fa::kThreads), 0, st, a);
           return;
         }
       }

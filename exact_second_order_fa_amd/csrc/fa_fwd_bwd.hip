@@ -51,8 +51,8 @@ __device__ inline f32x16 mfma_init_a(bf16x8 a, bf16x8 b, const f32x16& c) {
 // comes from one shared generator call per lane (DropRow), issued behind the
 // score MFMAs of the next sub-tile.
 // WPE: waves per SIMD (2; 3 for the d = 64 instances with 64-key tiles, 122
-// registers, 162 with the mask, and 33 KB of LDS a workgroup: three
-// workgroups per CU).
+// registers, 162 with the mask, and the d = 128 one with 32-key tiles, 166;
+// each 33 KB of LDS a workgroup: three workgroups per CU).
 // Largest partial row sum (16 exponentials of one lane) accepted against a
 // stale reference maximum; it bounds every exponential by 2^16.
 constexpr float kLazyBound = 65536.0f;
