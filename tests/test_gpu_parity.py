@@ -339,19 +339,20 @@ def test_binding_rejects_bad_arguments_before_launch():
     assert bool((sentinel == 7.0).all())
 
 
-@pytest.mark.parametrize("d,causal", [(64, False), (64, True), (128, False), (128, True)])
-def test_three_wave_forward_ragged(d, causal):
+@pytest.mark.parametrize("d,causal,layout", [(64, False, "bhnd"), (64, True, "bhnd"), (128, False, "bhnd"),
+                                             (128, True, "bhnd"), (64, False, "bnhd"), (128, True, "bnhd")])
+def test_three_wave_forward_ragged(d, causal, layout):
     """fa_fwd on a grid of 1536 row workgroups (48 heads x 32 row blocks) runs
     three waves per SIMD (64-key tiles at d = 64, 32-key tiles at d = 128);
-    N = 4000 leaves a ragged last tile.  O and L of every head against the
-    dense oracle."""
+    N = 4000 leaves a ragged last tile; "bnhd" passes strided head views.  O
+    and L of every head against the dense oracle."""
     import exact_second_order_fa_amd as fa
     from oracle import forward_dense
 
     B, H, N, seed = 1, 48, 4000, 610 + int(causal) + d
-    say(f"three-wave forward: B={B} H={H} N={N} d={d} causal={causal} seed={seed}")
+    say(f"three-wave forward: B={B} H={H} N={N} d={d} causal={causal} layout={layout} seed={seed}")
     raw, f64 = make_inputs(B, H, N, d, seed, "bf16")
-    t = to_device(raw, "bf16")
+    t = to_device(raw, "bf16", layout)
     o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], causal=causal)
     o, lse = host(o), host(lse)
     ref_o, ref_l = np.zeros((B, H, N, d)), np.zeros((B, H, N))
