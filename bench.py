@@ -576,7 +576,8 @@ def main():
         "frac_peak": round(value / peak, 4),
         "roofline": {"bound": "mfma", "kernel": "bob_pass1 (row pass)", "achieved": round(ach, 1),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                     "traffic": traffic, "flops_per_launch": pass1_flops},
+                     "traffic": traffic, "flops_per_launch": pass1_flops,
+                     "kernel_src_sha": kernel_source_sha()},
         "hbm": {"model_bytes_per_call": mb, "model_GBps": round(mb["total"] / (wall * 1e6), 1),
                 "pass1_counter_GBps": (round(traffic / (per[1] * 1e6), 1) if traffic else None),
                 "peak_GBps": 8000.0},
