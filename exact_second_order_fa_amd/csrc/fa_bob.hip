@@ -720,8 +720,9 @@ bob_pass2_dma_kernel(Args a) {
         const bf16x8 xq = rd_row<D, TS>(tq, rd, sub, ks);
         const bf16x8 xuq = rd_row<D, TS>(tuq, rd, sub, ks);
         const bf16x8 xd = rd_row<D, TS>(tdo, rd, sub, ks);
-        // The causal two-wave instance, short of registers, copies K and U_K
-        // back from AGPRs right before these: its MFMAs carry the wait.
+        // The causal and the dropout two-wave instances, short of registers,
+        // copy K and U_K back from AGPRs right before these: their MFMAs
+        // carry the wait.
         if constexpr (TWO && (CAUSAL || DROP)) {
           mfma_v_w(s, xq, kf[ks]);
           mfma_v_w(f, xuq, kf[ks]);
