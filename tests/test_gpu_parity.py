@@ -339,19 +339,24 @@ def test_binding_rejects_bad_arguments_before_launch():
     assert bool((sentinel == 7.0).all())
 
 
-@pytest.mark.parametrize("d,causal,layout", [(64, False, "bhnd"), (64, True, "bhnd"), (128, False, "bhnd"),
-                                             (128, True, "bhnd"), (64, False, "bnhd"), (128, True, "bnhd")])
-def test_three_wave_forward_ragged(d, causal, layout):
+@pytest.mark.parametrize("d,causal,layout,rising", [
+    (64, False, "bhnd", False), (64, True, "bhnd", False), (128, False, "bhnd", False), (128, True, "bhnd", False),
+    (64, False, "bnhd", False), (128, True, "bnhd", False), (64, False, "bhnd", True), (128, True, "bhnd", True)])
+def test_three_wave_forward_ragged(d, causal, layout, rising):
     """fa_fwd on a grid of 1536 row workgroups (48 heads x 32 row blocks) runs
     three waves per SIMD (64-key tiles at d = 64, 32-key tiles at d = 128);
-    N = 4000 leaves a ragged last tile; "bnhd" passes strided head views.  O
-    and L of every head against the dense oracle."""
+    N = 4000 leaves a ragged last tile; "bnhd" passes strided head views;
+    rising: key norms growing along the sequence and one late outlier (see
+    _rising_keys), so the lazy reference maximum moves.  O and L of every head
+    against the dense oracle."""
     import exact_second_order_fa_amd as fa
     from oracle import forward_dense
 
-    B, H, N, seed = 1, 48, 4000, 610 + int(causal) + d
-    say(f"three-wave forward: B={B} H={H} N={N} d={d} causal={causal} layout={layout} seed={seed}")
+    B, H, N, seed = 1, 48, 4000, 610 + int(causal) + d + 2 * int(rising)
+    say(f"three-wave forward: B={B} H={H} N={N} d={d} causal={causal} layout={layout} rising={rising} seed={seed}")
     raw, f64 = make_inputs(B, H, N, d, seed, "bf16")
+    if rising:
+        _rising_keys(raw, f64)
     t = to_device(raw, "bf16", layout)
     o, lse = fa.fa_fwd(t["q"], t["k"], t["v"], causal=causal)
     o, lse = host(o), host(lse)
